@@ -1,0 +1,40 @@
+"""CPU fp64 oracle for single-token decode attention (test infrastructure).
+
+This package is test infrastructure. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. The product package
+``kv_cache_decode_split_amd`` never imports it, and the two share no code: no kernels, headers,
+helpers, tables, constants or pre/post-processing. Only the seeded input generators
+(``kv_cache_decode_split_amd.workloads``, which hold none of the method's arithmetic) feed both.
+
+Modules
+-------
+decode_attention
+    The plain definition: materialised scores, max-subtracted softmax, weighted sum of V.
+online_softmax
+    The blockwise running-(m, l, O) recurrence and the merge of two running states, written in
+    the order the pages give them. Used to pin the exactness claim by brute force and as the
+    reference for the GPU merge step.
+fsum_reference
+    A second, pure-Python (math.fsum) implementation of the plain definition for tiny shapes.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against closed forms, invariants,
+brute force and the independent pure-Python implementation (no function is "parity unpinned").
+"""
+
+from .decode_attention import (  # noqa: F401
+    widen,
+    logical_rows,
+    stable_softmax,
+    attend_one,
+    decode_attention,
+    round_to_f32,
+)
+from .online_softmax import (  # noqa: F401
+    EMPTY_STATE,
+    block_state,
+    online_softmax,
+    merge_states,
+    merge_many,
+    finalize_state,
+)
+from .fsum_reference import decode_attention_fsum  # noqa: F401
