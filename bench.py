@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: achieved unique-KV HBM GB/s and decode-attention µs per step.
+
+One step is one pass of the whole path over one batch: for every layer of the workload, the
+split (streaming) kernel and the merge kernel through the C ABI. Inputs are seeded, synthetic
+and already resident in HBM when timing starts. The default workload is C2 (LLaMA-7B-shaped
+decode attention: B=8, h_q=h_kv=32, d=128, T=4096, bf16, 32 layers with their own caches,
+i.e. 32 launches of each kernel per step, 16 GiB of KV per step, far above the 256 MB
+last-level cache so every step streams from HBM).
+
+Measurement (Ch. 10 "System Model of Throughput and Latency" §8: warm up, time on the device
+with events, never time host submission):
+  * pass A: W warm-up steps, then K steps bracketed by device events on the launch stream, with
+    torch.cuda.synchronize() on both sides -> ms_per_step, value = unique KV bytes / step time;
+  * pass B: K more steps with events around every split-kernel launch -> that kernel's average
+    duration, and roofline.achieved = its unique KV bytes per launch / that duration;
+  * cpu_baseline: the fp64 oracle (oracle/) timed on the host on a bounded sample of the same
+    workload (whole (sequence, KV head) units of layer 0, about 15 s of CPU work).
+
+Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (unique KV bytes/time) + decode-attn µs/step"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_decode_split_amd", "csrc", "kv_attn_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per split launch from the committed counter summary, if it is current."""
+    path = os.path.join(PROFILES, f"traffic_split_kernel_{workload}.json")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(rec["hbm_bytes_per_launch"]), path
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's automatic plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run plain device copies of this size (counter calibration runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode-attention path has no multi-GPU component here).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_decode_split_amd import accounting as A
+    from kv_cache_decode_split_amd import kv_attn as K
+    from kv_cache_decode_split_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    spec = W.PRESETS[args.config]
+    layers = spec.layers
+    print(f"[bench] building {args.config} ({layers} layer(s)) on the GPU", file=sys.stderr, flush=True)
+    wls = [W.make_workload(spec, device="cuda", layer=l) for l in range(layers)]
+    outs = [torch.empty(w.q.shape, dtype=torch.float32, device="cuda") for w in wls]
+    probe = K.decode_call_for(wls[0], outs[0], num_splits=args.num_splits)
+    plan = probe.plan()
+    ws = (torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+          if plan["workspace_bytes"] else None)
+    calls = [K.decode_call_for(w, o, num_splits=args.num_splits, workspace=ws)
+             for w, o in zip(wls, outs)]
+    elem = 2 if spec.kv_dtype == "bf16" else 4
+    lens = [int(x) for x in wls[0].ctx_lens.cpu().tolist()]
+    kv_bytes_layer = A.unique_kv_read_bytes(lens, spec.num_kv_heads, spec.head_dim, elem)
+    kv_bytes_step = kv_bytes_layer * layers
+    flops_step = A.decode_attention_flops(lens, spec.num_q_heads, spec.head_dim) * layers
+
+    calib = None
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        calib = (torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1),
+                 torch.empty(n, dtype=torch.uint8, device="cuda"))
+
+    def step():
+        for c in calls:
+            c.decode()
+
+    # ---- pass A: whole steps -------------------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] pass A done: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # ---- pass B: per-launch events around the split kernel ---------------------------------------
+    evs = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for c in calls:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            c.split()
+            b.record()
+            c.merge()
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_us_avg = 1e3 * sum(split_ms) / len(split_ms)
+    print(f"[bench] pass B done: split kernel {split_us_avg:.1f} us/launch", file=sys.stderr, flush=True)
+
+    if calib is not None:  # plain copies of known size, for the counter-calibration runs
+        for _ in range(4):
+            calib[1].copy_(calib[0])
+        torch.cuda.synchronize()
+
+    finite = all(bool(torch.isfinite(o).all()) for o in outs)
+
+    # ---- CPU baseline: the oracle on a bounded sample --------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wls[0], spec, args.cpu_seconds, elem)
+
+    achieved = kv_bytes_layer / (split_us_avg * 1e-6) / 1e9
+    traffic, traffic_src = load_traffic(args.config)
+    value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "tokens_per_s": round(A.aggregate_tokens_per_s(spec.batch, ms_per_step * 1e-3), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec.name}: {spec.description}",
+            "batch": spec.batch, "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
+            "head_dim": spec.head_dim, "max_ctx_len": max(lens), "sum_ctx_len": sum(lens),
+            "layers": layers, "kv_dtype": spec.kv_dtype, "q_dtype": spec.q_dtype,
+            "paged": spec.paged, "layout": spec.layout,
+            "unique_kv_bytes_per_step": kv_bytes_step, "flops_per_step": flops_step,
+            "plan": {k: plan[k] for k in ("num_splits", "split_len", "grid_split", "grid_merge",
+                                          "kernel_variant", "num_cus")},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes_layer,
+            "avg_launch_us": round(split_us_avg, 2),
+            "launches_timed": len(split_ms),
+        },
+        "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "outputs_finite": finite,
+        "cpu_baseline": cpu,
+    }
+    if traffic is None:
+        line["roofline"]["traffic_note"] = traffic_src
+    print(json.dumps(line), flush=True)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, spec, budget_s, elem):
+    """The oracle, as it stands, on whole (sequence, KV head) units of layer 0 until the time
+    budget is spent (at least one unit). Returns unique-KV GB/s of the oracle."""
+    from kv_cache_decode_split_amd import workloads as W
+    from oracle import decode_attention
+
+    units = [(b, h) for b in range(spec.batch) for h in range(spec.num_kv_heads)]
+    lens = w.ctx_lens.cpu().tolist()
+    done_bytes, spent, n = 0, 0.0, 0
+    for b, h in units:
+        v = W.oracle_sample(w, [b], [h])  # host copy, outside the timed region
+        t0 = time.perf_counter()
+        decode_attention(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
+                         block_size=v["block_size"] if v["block_table"] is not None else None)
+        spent += time.perf_counter() - t0
+        done_bytes += 2 * int(lens[b]) * spec.head_dim * elem
+        n += 1
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {len(units)} (sequence, KV head) units of layer 0 of {spec.name} "
+                  f"({done_bytes} unique KV bytes, {spent:.1f} s)",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+/*
+ * kv_attn.h — C ABI of the split-KV decode-attention library for MI355X (gfx950).
+ *
+ * One decode step of attention: for every sequence b and query head h,
+ *
+ *     out[b][h][:] = softmax(scale * q[b][h] . K_b^T) . V_b
+ *
+ * over the ctx_lens[b] positions held in the KV cache for the KV head that query head h reads.
+ * This is the operation of one decode step in Ch. 19 "Inference Systems and Performance
+ * Engineering" (第19章 推理系统与性能工程) §19.4.1, computed with the blockwise online-softmax
+ * recurrence of §19.6.2 / §19.6.3 so the score row never leaves the chip. The cache may be
+ * paged (§19.7.3: fixed-size blocks reached through a per-sequence block table). Query heads
+ * share KV heads in groups (GQA) and each shared KV element is read from HBM once for the whole
+ * group, the unique-KV assumption of Ch. 10 "System Model of Throughput and Latency"
+ * (第十章 吞吐与延迟的系统模型) §4 and §5. The positions of a sequence are split across
+ * workgroups; each split produces a running state (m, l, O) and a second pass merges them.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named as device pointers must point to device memory (or memory the device can
+ *   read/write); host pointers to host memory. The library allocates nothing and frees
+ *   nothing; the caller owns every buffer.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued
+ *   asynchronously on it; no entry point synchronises unless the environment variable
+ *   KV_ATTN_DEBUG=1 is set (then inputs are validated on the host and the stream is
+ *   synchronised after the launch to report errors).
+ * - Every argument the host can see is validated before any HIP call; on an invalid argument
+ *   nothing is launched and the status says why. Contents of device-resident arrays (ctx_lens,
+ *   block_table) are not validated on the fast path; see kv_attn_validate_host.
+ * - Entry points are thread-safe: the only shared state is a per-device cache of the compute
+ *   unit count, filled once.
+ * - GQA grouping: with g = num_q_heads / num_kv_heads, query head h reads KV head h / g.
+ * - ctx_lens[b] counts every position attended, the current token included (the caller has
+ *   already appended it); there is no mask inside those positions. ctx_lens[b] == 0 gives an
+ *   output row of zeros.
+ */
+#ifndef KV_ATTN_H_
+#define KV_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_ATTN_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum kv_attn_status {
+  KV_ATTN_OK = 0,
+  KV_ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  KV_ATTN_ERR_SHAPE = 2,       /* inconsistent sizes (B, heads, block size, lengths) */
+  KV_ATTN_ERR_UNSUPPORTED = 3, /* head_dim, group size, dtype or alignment not supported */
+  KV_ATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the plan needs */
+  KV_ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error (launch or query) */
+  KV_ATTN_ERR_TABLE = 6,       /* validator: ctx_lens / block_table content out of range */
+  KV_ATTN_ERR_VALUE = 7        /* an invalid scalar (non-finite scale, negative count) */
+} kv_attn_status;
+
+/* Storage types of q and of the KV cache. */
+typedef enum kv_attn_dtype {
+  KV_ATTN_F32 = 0,
+  KV_ATTN_BF16 = 1
+} kv_attn_dtype;
+
+/*
+ * Problem description.
+ *
+ * q        : [batch, num_q_heads, head_dim], contiguous, q_dtype.
+ * out      : [batch, num_q_heads, head_dim], contiguous, fp32.
+ * k_cache,
+ * v_cache  : element (block, token-in-block, kv_head, i) lives at
+ *              base + block*stride_block + token*stride_token + kv_head*stride_head + i
+ *            (elements of kv_dtype; the head_dim stride is 1). Both [blocks, block_size,
+ *            h_kv, d] ("token major") and [blocks, h_kv, block_size, d] ("head major") are
+ *            expressible; head major keeps the rows one (sequence, KV head) streams adjacent.
+ * Paged cache (block_table != NULL): logical position t of sequence b is token
+ *            t % block_size of physical block block_table[b * max_blocks_per_seq + t / block_size].
+ *            Several sequences may point at the same physical block (prefix sharing); the cache
+ *            is only read.
+ * Contiguous cache (block_table == NULL): sequence b is "block" b and position t is token t;
+ *            block_size is then the token capacity of one sequence slot.
+ */
+typedef struct kv_attn_params {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_heads;        /* h_q >= 1 */
+  int32_t num_kv_heads;       /* h_kv >= 1, h_q % h_kv == 0, 1 <= h_q / h_kv <= 16 */
+  int32_t head_dim;           /* d: 64 or 128 */
+  int32_t block_size;         /* paged: power of two >= 16; contiguous: slot capacity >= max_ctx_len */
+  int32_t max_blocks_per_seq; /* paged: row length of block_table (>= 1); ignored if contiguous */
+  int32_t max_ctx_len;        /* host-known upper bound of every ctx_lens[b] (>= 0); sizes the grid */
+  int32_t num_splits;         /* 0 = automatic; > 0 requests that many splits per sequence */
+  int32_t q_dtype;            /* kv_attn_dtype */
+  int32_t kv_dtype;           /* kv_attn_dtype */
+  float scale;                /* score scale; 0 means 1/sqrt(head_dim) */
+  int32_t reserved;           /* must be 0 */
+  int64_t num_blocks;         /* physical blocks in the caches (contiguous: batch); validator bound */
+  int64_t k_stride_block, k_stride_token, k_stride_head; /* elements, >= 0 */
+  int64_t v_stride_block, v_stride_token, v_stride_head; /* elements, >= 0 */
+} kv_attn_params;
+
+/* The launch plan kv_attn_decode will use for a problem (split planning). */
+typedef struct kv_attn_plan {
+  int32_t num_splits;       /* S: splits per (sequence, KV head) */
+  int32_t split_len;        /* positions per split, a multiple of 16 */
+  int32_t grid_split;       /* workgroups of the split kernel: batch * num_kv_heads * S */
+  int32_t grid_merge;       /* workgroups of the merge kernel (0 when S == 1) */
+  int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores */
+  int32_t group_padded;     /* compiled group width (power of two >= g) */
+  int32_t num_cus;          /* compute units the plan was made for */
+  int32_t reserved;
+  uint64_t workspace_bytes; /* workspace kv_attn_decode needs (0 when S == 1) */
+  uint64_t ml_offset;       /* byte offset of the (m, l) array inside the workspace (S > 1) */
+} kv_attn_plan;
+
+/* ABI version of the loaded library (KV_ATTN_ABI_VERSION it was built with). */
+int32_t kv_attn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* kv_attn_status_string(int32_t status);
+
+/*
+ * Plan the launch for `p` as if on a device with `num_cus` compute units (0 = query the
+ * current HIP device). Validates `p` exactly as kv_attn_decode does (pointers aside). Split
+ * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
+ * workgroups number about 8 per compute unit, each split spans 16..256 tiles, and a
+ * caller-given num_splits overrides the count. Writes *plan only on KV_ATTN_OK.
+ */
+kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_attn_plan* plan);
+
+/* Workspace bytes kv_attn_decode needs for `p` on the current device; 0 if none or if `p`
+ * is invalid. */
+size_t kv_attn_workspace_size(const kv_attn_params* p);
+
+/*
+ * Decode attention for one step (see the top of this file for the computation).
+ *
+ * q, k_cache, v_cache : device, layouts above, 16-byte aligned; every stride times the
+ *                       element size must be a multiple of 16 bytes.
+ * block_table         : device int32 [batch, max_blocks_per_seq], or NULL for a contiguous cache.
+ *                       Entries past ceil(ctx_lens[b] / block_size) are never read.
+ * ctx_lens            : device int32 [batch]; contract 0 <= ctx_lens[b] <= max_ctx_len (values
+ *                       outside are clamped into that range).
+ * out                 : device fp32 [batch, num_q_heads, head_dim]; must not alias any input.
+ * workspace           : device scratch of at least kv_attn_workspace_size(p) bytes when the plan
+ *                       has more than one split (may be NULL otherwise); contents need no
+ *                       initialisation and are left unspecified.
+ * Returns KV_ATTN_OK once the kernels are enqueued.
+ */
+kv_attn_status kv_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                              const kv_attn_params* p, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * The two passes of kv_attn_decode, separately (same arguments and checks; calling
+ * kv_attn_decode_split then kv_attn_decode_merge with the same p, workspace and stream is
+ * exactly kv_attn_decode).
+ *
+ * kv_attn_decode_split: the streaming pass. With a one-split plan it writes `out` and the merge
+ * pass is a no-op. Otherwise it leaves every split's running state in the workspace: the
+ * unnormalised sums O at byte offset 0 as fp32 [batch * num_q_heads, S, head_dim] and (m, l) at
+ * byte offset plan.ml_offset as fp32 [batch * num_q_heads, S, 2], m being a base-2 maximum (see
+ * kv_attn_merge). Split s of sequence b covers positions [s * split_len, (s+1) * split_len) of
+ * that sequence; splits starting at or past ctx_lens[b] are not written.
+ * kv_attn_decode_merge: the merge pass over a workspace the split pass filled; it merges, for
+ * row (b, h), the first ceil(ctx_lens[b] / split_len) splits into out.
+ */
+kv_attn_status kv_attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                                    const kv_attn_params* p, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+kv_attn_status kv_attn_decode_merge(const int32_t* ctx_lens, float* out, const kv_attn_params* p,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge per-split running states into outputs (the second pass of kv_attn_decode, exposed
+ * for callers that produce split states elsewhere, e.g. position ranges held by different
+ * devices). The merge rescales each state to the common maximum, as in the online-softmax
+ * recurrence of Ch. 19 §19.6.2 applied with a whole split state in place of one block:
+ *
+ *     M = max_s m_s;  w_s = 2^(m_s - M);  out = (sum_s w_s O_s) / (sum_s w_s l_s)
+ *
+ * o_partial  : device fp32 [rows, num_splits, head_dim], unnormalised sums O_s.
+ * ml_partial : device fp32 [rows, num_splits, 2] holding (m_s, l_s); m_s is a maximum of
+ *              base-2 scaled scores (natural-log logits times log2(e)); a state with
+ *              m_s = -inf and l_s = 0 is empty and is skipped.
+ * num_valid  : device int32 [rows] (only the first num_valid[r] splits of row r are merged,
+ *              clamped to [0, num_splits]) or NULL (all splits).
+ * out        : device fp32 [rows, head_dim]; a row with no non-empty state is written as zeros.
+ * head_dim   : 64 or 128.
+ */
+kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
+                             const int32_t* num_valid, float* out, int32_t rows,
+                             int32_t num_splits, int32_t head_dim, void* stream);
+
+/*
+ * Host-side check of the device-resident inputs' contents (debug aid; runs on the CPU and
+ * touches no device): every 0 <= ctx_lens[b] <= max_ctx_len and, for a paged cache
+ * (block_table != NULL), every entry 0 <= block_table[b][i] < num_blocks for
+ * i < ceil(ctx_lens[b] / block_size). Both arrays are host copies. Returns KV_ATTN_ERR_TABLE
+ * on the first violation, KV_ATTN_OK otherwise (after validating `p` as kv_attn_get_plan does).
+ */
+kv_attn_status kv_attn_validate_host(const int32_t* block_table, const int32_t* ctx_lens,
+                                     const kv_attn_params* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KV_ATTN_H_ */

@@ -1,0 +1,252 @@
+// C entry points that touch the HIP runtime: planning on the current device, decode, merge.
+// Argument checks run before any HIP call; see include/kv_attn.h for the contract.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <vector>
+
+#include "kv_attn_internal.h"
+
+namespace kvattn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+// Compute units of the current device, cached per device. Returns 0 on a HIP error.
+int current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices && cus > 0) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool debug_mode() {
+  const char* e = getenv("KV_ATTN_DEBUG");
+  return e != nullptr && strcmp(e, "1") == 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+// KV_ATTN_DEBUG=1: copy the device-resident tables to the host and validate them.
+kv_attn_status debug_validate(const int32_t* block_table, const int32_t* ctx_lens,
+                              const kv_attn_params* p, hipStream_t stream) {
+  std::vector<int32_t> ctx(p->batch);
+  std::vector<int32_t> table;
+  if (hipStreamSynchronize(stream) != hipSuccess) return KV_ATTN_ERR_HIP;
+  if (hipMemcpy(ctx.data(), ctx_lens, sizeof(int32_t) * ctx.size(), hipMemcpyDeviceToHost) != hipSuccess)
+    return KV_ATTN_ERR_HIP;
+  if (block_table != nullptr) {
+    table.resize(size_t(p->batch) * p->max_blocks_per_seq);
+    if (hipMemcpy(table.data(), block_table, sizeof(int32_t) * table.size(), hipMemcpyDeviceToHost) !=
+        hipSuccess)
+      return KV_ATTN_ERR_HIP;
+  }
+  return kv_attn_validate_host(block_table != nullptr ? table.data() : nullptr, ctx.data(), p);
+}
+
+}  // namespace
+}  // namespace kvattn
+
+extern "C" {
+
+kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_attn_plan* plan) {
+  if (p == nullptr || plan == nullptr) return KV_ATTN_ERR_NULL;
+  if (num_cus < 0) return KV_ATTN_ERR_VALUE;
+  const kv_attn_status st = kvattn::validate_params(p);
+  if (st != KV_ATTN_OK) return st;
+  int cus = num_cus;
+  if (cus == 0) {
+    if (kvattn::fault_injected("query")) return KV_ATTN_ERR_HIP;
+    cus = kvattn::current_cu_count();
+    if (cus <= 0) return KV_ATTN_ERR_HIP;
+  }
+  kvattn::Plan pl;
+  const kv_attn_status ps = kvattn::make_plan(p, cus, &pl);
+  if (ps != KV_ATTN_OK) return ps;
+  plan->num_splits = pl.num_splits;
+  plan->split_len = pl.split_tiles * kvattn::kTile;
+  plan->grid_split = int32_t(pl.grid_split);
+  plan->grid_merge = int32_t(pl.grid_merge);
+  plan->kernel_variant = pl.variant;
+  plan->group_padded = pl.group_padded;
+  plan->num_cus = cus;
+  plan->reserved = 0;
+  plan->workspace_bytes = pl.workspace_bytes;
+  plan->ml_offset = pl.num_splits > 1 ? pl.o_part_bytes : 0;
+  return KV_ATTN_OK;
+}
+
+size_t kv_attn_workspace_size(const kv_attn_params* p) {
+  kv_attn_plan plan;
+  if (kv_attn_get_plan(p, 0, &plan) != KV_ATTN_OK) return 0;
+  return size_t(plan.workspace_bytes);
+}
+
+}  // extern "C"
+
+namespace kvattn {
+namespace {
+
+constexpr int kPassSplit = 1;
+constexpr int kPassMerge = 2;
+
+// Shared body of kv_attn_decode / _split / _merge: validation, planning, then the passes in
+// `passes`. Every host-side check runs before the first HIP call.
+kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                           const kv_attn_params* p, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (p == nullptr || ctx_lens == nullptr || out == nullptr) return KV_ATTN_ERR_NULL;
+  if ((passes & kPassSplit) && (q == nullptr || k_cache == nullptr || v_cache == nullptr))
+    return KV_ATTN_ERR_NULL;
+  const bool paged = block_table != nullptr;
+  kv_attn_status st = (passes & kPassSplit) ? validate_layout(p, paged) : validate_params(p);
+  if (st != KV_ATTN_OK) return st;
+  if ((passes & kPassSplit) &&
+      (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)))
+    return KV_ATTN_ERR_UNSUPPORTED;
+
+  if (fault_injected("query")) return KV_ATTN_ERR_HIP;
+  const int cus = current_cu_count();
+  if (cus <= 0) return KV_ATTN_ERR_HIP;
+  Plan plan;
+  st = make_plan(p, cus, &plan);
+  if (st != KV_ATTN_OK) return st;
+  if (plan.num_splits > 1) {
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return KV_ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KV_ATTN_ERR_UNSUPPORTED;
+  }
+  if (fault_injected("launch")) return KV_ATTN_ERR_HIP;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((passes & kPassSplit) && debug_mode()) {
+    st = debug_validate(block_table, ctx_lens, p, s);
+    if (st != KV_ATTN_OK) return st;
+  }
+  float* o_part = plan.num_splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  float* ml_part = plan.num_splits > 1
+                       ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.o_part_bytes)
+                       : nullptr;
+
+  if (passes & kPassSplit) {
+    SplitArgs a;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.block_table = block_table;
+    a.ctx_lens = ctx_lens;
+    a.out = out;
+    a.o_part = o_part;
+    a.ml_part = ml_part;
+    a.k_sb = p->k_stride_block;
+    a.k_st = p->k_stride_token;
+    a.k_sh = p->k_stride_head;
+    a.v_sb = p->v_stride_block;
+    a.v_st = p->v_stride_token;
+    a.v_sh = p->v_stride_head;
+    a.h_q = p->num_q_heads;
+    a.h_kv = p->num_kv_heads;
+    a.group = p->num_q_heads / p->num_kv_heads;
+    a.bs_log2 = paged ? log2_exact(p->block_size) : 0;
+    a.max_blocks = paged ? p->max_blocks_per_seq : 0;
+    a.max_ctx = p->max_ctx_len;
+    a.split_tiles = plan.split_tiles;
+    a.num_splits = plan.num_splits;
+    const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
+    a.scale_log2 = float(scale * 1.4426950408889634);  // log2(e)
+    if (launch_split(a, plan, p->head_dim, paged, p->q_dtype == KV_ATTN_BF16,
+                     p->kv_dtype == KV_ATTN_BF16, stream) != 0)
+      return KV_ATTN_ERR_HIP;
+  }
+  if ((passes & kPassMerge) && plan.num_splits > 1) {
+    MergeArgs m;
+    m.o_part = o_part;
+    m.ml_part = ml_part;
+    m.num_valid = nullptr;
+    m.ctx_lens = ctx_lens;
+    m.out = out;
+    m.rows = p->batch * p->num_q_heads;
+    m.num_splits = plan.num_splits;
+    m.h_q = p->num_q_heads;
+    m.split_len = plan.split_tiles * kTile;
+    m.max_ctx = p->max_ctx_len;
+    if (launch_merge(m, p->head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
+  }
+  if (debug_mode()) {
+    if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) return KV_ATTN_ERR_HIP;
+  }
+  return KV_ATTN_OK;
+}
+
+}  // namespace
+}  // namespace kvattn
+
+extern "C" {
+
+kv_attn_status kv_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                              const kv_attn_params* p, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return kvattn::decode_impl(kvattn::kPassSplit | kvattn::kPassMerge, q, k_cache, v_cache,
+                             block_table, ctx_lens, out, p, workspace, workspace_bytes, stream);
+}
+
+kv_attn_status kv_attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                                    const kv_attn_params* p, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return kvattn::decode_impl(kvattn::kPassSplit, q, k_cache, v_cache, block_table, ctx_lens, out,
+                             p, workspace, workspace_bytes, stream);
+}
+
+kv_attn_status kv_attn_decode_merge(const int32_t* ctx_lens, float* out, const kv_attn_params* p,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return kvattn::decode_impl(kvattn::kPassMerge, nullptr, nullptr, nullptr, nullptr, ctx_lens, out,
+                             p, workspace, workspace_bytes, stream);
+}
+
+kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
+                             const int32_t* num_valid, float* out, int32_t rows,
+                             int32_t num_splits, int32_t head_dim, void* stream) {
+  if (o_partial == nullptr || ml_partial == nullptr || out == nullptr) return KV_ATTN_ERR_NULL;
+  if (rows < 1 || num_splits < 1) return KV_ATTN_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return KV_ATTN_ERR_UNSUPPORTED;
+  if (int64_t(rows) * num_splits > (int64_t(1) << 40)) return KV_ATTN_ERR_SHAPE;
+  if (kvattn::fault_injected("launch")) return KV_ATTN_ERR_HIP;
+  kvattn::MergeArgs m;
+  m.o_part = o_partial;
+  m.ml_part = ml_partial;
+  m.num_valid = num_valid;
+  m.ctx_lens = nullptr;
+  m.out = out;
+  m.rows = rows;
+  m.num_splits = num_splits;
+  m.h_q = 1;
+  m.split_len = 1;
+  m.max_ctx = 0;
+  if (kvattn::launch_merge(m, head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
+  if (kvattn::debug_mode()) {
+    if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess ||
+        hipGetLastError() != hipSuccess)
+      return KV_ATTN_ERR_HIP;
+  }
+  return KV_ATTN_OK;
+}
+
+}  // extern "C"

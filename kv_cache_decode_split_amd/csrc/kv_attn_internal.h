@@ -1,0 +1,86 @@
+// Internal interfaces between the host layer and the kernels (not part of the C ABI).
+#ifndef KV_ATTN_INTERNAL_H_
+#define KV_ATTN_INTERNAL_H_
+
+#include <stdint.h>
+
+#include "kv_attn.h"
+
+namespace kvattn {
+
+// Positions per tile: one MFMA row block, and one 16-token block of a paged cache.
+constexpr int kTile = 16;
+// Waves per split workgroup; each wave streams every kWaves-th tile of the split.
+constexpr int kWaves = 4;
+constexpr int kSplitThreads = 64 * kWaves;
+// Rows (sequence, query head) merged per merge workgroup: one wave each.
+constexpr int kMergeRowsPerBlock = 4;
+// Split planning constants (see make_plan).
+constexpr int kMinSplitTiles = 16;     // a split spans at least 256 positions ...
+constexpr int kMaxSplitTiles = 256;    // ... and at most 4096 positions
+constexpr int kWorkgroupsPerCu = 8;    // target split workgroups per compute unit
+constexpr int kMaxSplits = 4096;
+
+// Everything the split kernel needs, by value.
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;  // nullptr: contiguous cache
+  const int32_t* ctx_lens;
+  float* out;                  // final output (num_splits == 1)
+  float* o_part;               // [B, h_q, S, d] unnormalised sums (num_splits > 1)
+  float* ml_part;              // [B, h_q, S, 2] (m in base-2 units, l)
+  int64_t k_sb, k_st, k_sh;    // element strides of the K cache
+  int64_t v_sb, v_st, v_sh;
+  int32_t h_q;
+  int32_t h_kv;
+  int32_t group;               // g = h_q / h_kv
+  int32_t bs_log2;             // paged: log2(block_size); unused when contiguous
+  int32_t max_blocks;          // paged: row length of block_table
+  int32_t max_ctx;             // ctx_lens are clamped into [0, max_ctx]
+  int32_t split_tiles;         // tiles per split
+  int32_t num_splits;          // S
+  float scale_log2;            // scale * log2(e)
+};
+
+struct MergeArgs {
+  const float* o_part;         // [rows, S, d]
+  const float* ml_part;        // [rows, S, 2]
+  const int32_t* num_valid;    // [rows] or nullptr
+  const int32_t* ctx_lens;     // decode path: valid splits = ceil(ctx / split_len) (nullptr otherwise)
+  float* out;                  // [rows, d]
+  int32_t rows;
+  int32_t num_splits;
+  int32_t h_q;                 // decode path: row / h_q is the sequence
+  int32_t split_len;           // decode path
+  int32_t max_ctx;             // decode path: clamp of ctx_lens
+};
+
+struct Plan {
+  int32_t num_splits;
+  int32_t split_tiles;
+  int32_t group_padded;
+  int32_t variant;  // 0: vector fp32 path, 1: MFMA scores
+  int64_t grid_split;
+  int64_t grid_merge;
+  uint64_t workspace_bytes;
+  uint64_t o_part_bytes;  // offset of ml_part inside the workspace
+};
+
+// Host-only helpers (kv_attn_plan.cpp; no HIP calls).
+kv_attn_status validate_params(const kv_attn_params* p);
+// Checks that depend on whether the cache is paged (block_table present) or contiguous.
+kv_attn_status validate_layout(const kv_attn_params* p, bool paged);
+kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan);
+int32_t padded_group(int32_t g);
+bool fault_injected(const char* where);  // KV_ATTN_FAULT=<where>: simulate a HIP failure
+
+// Kernel launchers (kv_attn_kernels.hip); return a hipError_t value (0 = success).
+int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, bool q_bf16,
+                 bool kv_bf16, void* stream);
+int launch_merge(const MergeArgs& a, int head_dim, void* stream);
+
+}  // namespace kvattn
+
+#endif  // KV_ATTN_INTERNAL_H_

@@ -1,0 +1,534 @@
+// Split-KV decode attention kernels for gfx950 (CDNA4, wave64).
+//
+// What is computed (Ch. 19 "Inference Systems and Performance Engineering" §19.4.1): for one
+// new query token per sequence, out = softmax(scale * q . K^T) . V over the sequence's cached
+// positions. The score row is never materialised: positions stream through in tiles and a
+// running state (m, l, O) is updated per tile with the online-softmax recurrence of §19.6.2
+// (new max, rescale factor c = 2^(m_old - m_new) applied to l and O, then the tile's
+// exponentials added), as in the tiled forward pass of §19.6.3 specialised to one query row.
+// Scores are kept in base-2 units (scale * log2 e folded in) so every exponential is a single
+// v_exp_f32; the base cancels between numerator and denominator.
+//
+// Work decomposition. One workgroup (4 waves) per (sequence b, KV head, split). A split is a
+// run of 16-position tiles; wave w streams tiles w, w+4, w+8, ... of the split with its own
+// running state, so no barrier is needed inside the streaming loop. At the end the four wave
+// states are merged through LDS (the same rescale-and-add step applied to whole states) and
+// either the normalised output (one split) or the split's (m, l, O) goes to global memory; a
+// second kernel merges splits. Every KV element of the group's KV head is loaded once and used
+// by all g query heads that share it (the unique-KV reuse Ch. 10 §4 assumes for GQA).
+//
+// Per-tile data paths:
+//  * bf16 q and KV (variant 1): scores come from the matrix cores. With A = the tile's 16 key
+//    rows and B = the group's query rows (zero-padded to 16 heads), a 16x16x32 bf16 MFMA chain
+//    over d produces S[token][head]; bf16 products are exact and accumulate in fp32.
+//  * any other dtype mix (variant 0): each row of 16 lanes holds one key row, each lane a
+//    d/16-element slice; partial dots are summed across the row with DPP.
+//  * Both variants accumulate P.V in fp32 on the vector ALUs: lane (r, q4) owns elements
+//    [r*d/16, (r+1)*d/16) of the value rows 4*q4 .. 4*q4+3 of the tile, and takes the
+//    probabilities it needs by DPP row broadcast (variant 1) or directly (variant 0).
+//
+// Loads are 64- to 128-bit per lane; the tile's key rows are 16 contiguous 64-byte pieces per
+// instruction (MFMA operand layout), value rows are whole 256-byte rows per 16 lanes. Tiles
+// are double-buffered in registers so the next tile's loads are in flight while the current
+// one is computed. Positions past the sequence end are never read: their row index is clamped
+// to the last valid row and the score is masked to -inf.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kv_attn_internal.h"
+
+namespace kvattn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDepth = 2;  // tiles in flight per wave
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;      // rotate right by 4 within a row of 16 lanes
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowNewBcast0 = 0x150; // row_newbcast:n, lane n of each row to the whole row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a row; every lane of the row gets the total.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowRor4>(x);
+  x += dpp<kDppRowRor8>(x);
+  return x;
+}
+
+// Value of lane J of this lane's row.
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp<kDppRowNewBcast0 + J>(x);
+}
+
+__device__ __forceinline__ float lane_xor(float x, int mask) { return __shfl_xor(x, mask); }
+
+// Raw per-lane slice of one row: BYTES = 8, 16 or 32.
+template <int BYTES>
+struct Seg {
+  uint32_t w[BYTES / 4];
+};
+
+template <int BYTES>
+__device__ __forceinline__ Seg<BYTES> load_seg(const char* p) {
+  Seg<BYTES> s;
+  if constexpr (BYTES == 8) {
+    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    s.w[0] = x[0];
+    s.w[1] = x[1];
+  } else {
+    static_for<0, BYTES / 16>([&](auto I) __attribute__((always_inline)) {
+      const u32x4_t x = reinterpret_cast<const u32x4_t*>(p)[I()];
+      s.w[4 * I() + 0] = x[0];
+      s.w[4 * I() + 1] = x[1];
+      s.w[4 * I() + 2] = x[2];
+      s.w[4 * I() + 3] = x[3];
+    });
+  }
+  return s;
+}
+
+// Exact widening of N stored elements to fp32 (bf16: the 16 bits become the high half).
+template <int N, bool BF16, int BYTES>
+__device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
+  if constexpr (BF16) {
+    static_assert(BYTES * 8 == N * 16, "segment size");
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      f[2 * i] = __uint_as_float(s.w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(s.w[i] & 0xffff0000u);
+    }
+  } else {
+    static_assert(BYTES == N * 4, "segment size");
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = __uint_as_float(s.w[i]);
+  }
+}
+
+// PAGED: 0 contiguous, 1 paged, 2 decided at run time (vector variant only).
+template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED>
+__global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(!MFMA || (Q_BF16 && KV_BF16), "matrix-core scores need bf16 q and KV");
+  constexpr int EPL = D / 16;                 // elements per lane of a 16-lane row
+  constexpr int KVB = KV_BF16 ? 2 : 4;        // bytes per KV element
+  constexpr int QB = Q_BF16 ? 2 : 4;
+  constexpr int SEG = EPL * KVB;              // bytes per lane per row
+  constexpr int KC = D / 32;                  // MFMA k-chunks (32 bf16 each)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  const int S = a.num_splits;
+  const int split = blockIdx.x % S;
+  const int unit = blockIdx.x / S;
+  const int kvh = unit % a.h_kv;
+  const int b = unit / a.h_kv;
+  const int g = a.group;
+  const bool paged = PAGED == 2 ? (a.block_table != nullptr) : (PAGED == 1);
+
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  const int ntiles = (ctx + kTile - 1) / kTile;
+  const int t_begin = split * a.split_tiles;
+  const int64_t q_row0 = int64_t(b) * a.h_q + int64_t(kvh) * g;  // first query head of the group
+  if (t_begin >= ntiles) {
+    // Only an empty sequence reaches here with one split: its rows are defined as zeros.
+    if (S == 1) {
+      for (int idx = threadIdx.x; idx < g * D; idx += kSplitThreads)
+        a.out[(q_row0 + idx / D) * D + idx % D] = 0.f;
+    }
+    return;
+  }
+  const int t_end = min(t_begin + a.split_tiles, ntiles);
+  const int first = t_begin + wave;                                   // this wave's first tile
+  const int n_w = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
+
+  // ---- query rows, loaded once ------------------------------------------------------------
+  bf16x8_t qb[KC];      // MFMA B operand: head r16, elements c*32 + q4*8 .. +8
+  float qf[G][EPL];     // vector path: every head, elements r16*EPL .. +EPL
+  if constexpr (MFMA) {
+    const char* qbase = reinterpret_cast<const char*>(a.q);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (r16 < g)
+        x = *reinterpret_cast<const u32x4_t*>(qbase + ((q_row0 + r16) * D + c * 32 + q4 * 8) * 2);
+      qb[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  } else {
+    const char* qbase = reinterpret_cast<const char*>(a.q);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (j < g) {
+        const Seg<EPL * QB> s = load_seg<EPL * QB>(qbase + ((q_row0 + j) * D + r16 * EPL) * QB);
+        widen<EPL, Q_BF16>(s, qf[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qf[j][e] = 0.f;
+      }
+    }
+  }
+
+  // ---- running state -------------------------------------------------------------------------
+  // Variant 1: m_run / l_run belong to head r16 (l_run summed over this lane's 4 positions).
+  // Variant 0: per head arrays, uniform across the wave (m) or across the row (l).
+  float m_run = neg_inf(), l_run = 0.f;
+  float m_v[G], l_v[G];
+  float O[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m_v[j] = neg_inf();
+    l_v[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) O[j][e] = 0.f;
+  }
+
+  // ---- tile addressing -------------------------------------------------------------------------
+  const char* kbase = reinterpret_cast<const char*>(a.k);
+  const char* vbase = reinterpret_cast<const char*>(a.v);
+  int bt_vec = 0, bt_base = -64;  // block ids of this wave's tiles bt_base .. bt_base+63, one per lane
+
+  struct Frag {
+    u32x4_t kc[KC];      // variant 1: key row r16, 32-element chunks
+    Seg<SEG> kr[4];      // variant 0: key rows 4*q4+i
+    Seg<SEG> vr[4];      // value rows 4*q4+i
+  };
+
+  auto load_tile = [&](int k, Frag& f) __attribute__((always_inline)) {
+    const int tile = first + kWaves * k;
+    const int p0 = tile * kTile;
+    const int last = ctx - 1 - p0;  // >= 0: rows past it are clamped to it
+    int64_t koff, voff;             // element offset of tile row 0
+    if (paged) {
+      if (k - bt_base >= 64) {
+        const int kk = (k & ~63) + lane;
+        int blk = 0;
+        if (kk < n_w)
+          blk = a.block_table[int64_t(b) * a.max_blocks + (((first + kWaves * kk) * kTile) >> a.bs_log2)];
+        bt_vec = blk;
+        bt_base = k & ~63;
+      }
+      const int blk = __builtin_amdgcn_readlane(bt_vec, k - bt_base);
+      const int slot0 = p0 & ((1 << a.bs_log2) - 1);
+      koff = int64_t(blk) * a.k_sb + int64_t(slot0) * a.k_st + int64_t(kvh) * a.k_sh;
+      voff = int64_t(blk) * a.v_sb + int64_t(slot0) * a.v_st + int64_t(kvh) * a.v_sh;
+    } else {
+      koff = int64_t(b) * a.k_sb + int64_t(p0) * a.k_st + int64_t(kvh) * a.k_sh;
+      voff = int64_t(b) * a.v_sb + int64_t(p0) * a.v_st + int64_t(kvh) * a.v_sh;
+    }
+    const char* kt = kbase + koff * KVB;
+    const char* vt = vbase + voff * KVB;
+    if constexpr (MFMA) {
+      const int row = min(r16, last);
+      const char* kr = kt + (int64_t(row) * a.k_st + q4 * 8) * 2;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) f.kc[c] = *reinterpret_cast<const u32x4_t*>(kr + c * 64);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = min(4 * q4 + i, last);
+        f.kr[i] = load_seg<SEG>(kt + (int64_t(row) * a.k_st + r16 * EPL) * KVB);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(4 * q4 + i, last);
+      f.vr[i] = load_seg<SEG>(vt + (int64_t(row) * a.v_st + r16 * EPL) * KVB);
+    }
+  };
+
+  auto compute_tile = [&](int k, const Frag& f) __attribute__((always_inline)) {
+    const int tile = first + kWaves * k;
+    const int nvalid = ctx - tile * kTile;  // positions 0 .. nvalid-1 of the tile are real
+    float p[4][G];                          // variant 0: probabilities of rows 4*q4+i
+    float pm[4];                            // variant 1: probability of (row 4*q4+i, head r16)
+    bool rescale;
+    if constexpr (MFMA) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.kc[c]), qb[c],
+                                                      acc, 0, 0, 0);
+      // acc[r] = score of tile row 4*q4 + r for head r16.
+      float s[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = (4 * q4 + r < nvalid) ? acc[r] * a.scale_log2 : neg_inf();
+      float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mt = fmaxf(mt, lane_xor(mt, 16));
+      mt = fmaxf(mt, lane_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float c = exp2_fast(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pm[r] = exp2_fast(s[r] - m_new);
+      l_run = c * l_run + ((pm[0] + pm[1]) + (pm[2] + pm[3]));
+      m_run = m_new;
+      rescale = __any(r16 < G && c != 1.0f);
+      if (rescale) {
+        static_for<0, G>([&](auto J) __attribute__((always_inline)) {
+          const float cj = row_bcast<J()>(c);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) O[J()][e] *= cj;
+        });
+      }
+    } else {
+      float s[4][G];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float kf[EPL];
+        widen<EPL, KV_BF16>(f.kr[i], kf);
+        const bool valid = 4 * q4 + i < nvalid;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float x = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) x = fmaf(qf[j][e], kf[e], x);
+          x = row_sum16(x);
+          s[i][j] = valid ? x * a.scale_log2 : neg_inf();
+        }
+      }
+      bool any_change = false;
+      float cv[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float mt = fmaxf(fmaxf(s[0][j], s[1][j]), fmaxf(s[2][j], s[3][j]));
+        mt = fmaxf(mt, lane_xor(mt, 16));
+        mt = fmaxf(mt, lane_xor(mt, 32));
+        const float m_new = fmaxf(m_v[j], mt);
+        cv[j] = exp2_fast(m_v[j] - m_new);
+        m_v[j] = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i][j] = exp2_fast(s[i][j] - m_new);
+        l_v[j] = cv[j] * l_v[j] + ((p[0][j] + p[1][j]) + (p[2][j] + p[3][j]));
+        any_change |= cv[j] != 1.0f;
+      }
+      rescale = __any(any_change);
+      if (rescale) {
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) O[j][e] *= cv[j];
+      }
+    }
+    // P.V for value rows 4*q4 .. 4*q4+3, elements r16*EPL .. +EPL, every head of the group.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float vf[EPL];
+      widen<EPL, KV_BF16>(f.vr[i], vf);
+      static_for<0, G>([&](auto J) __attribute__((always_inline)) {
+        float pj;
+        if constexpr (MFMA)
+          pj = row_bcast<J()>(pm[i]);
+        else
+          pj = p[i][J()];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) O[J()][e] = fmaf(pj, vf[e], O[J()][e]);
+      });
+    }
+  };
+
+  // ---- streaming loop: kDepth tiles in flight ------------------------------------------------
+  Frag buf[kDepth];
+  static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+    if (P() < n_w) load_tile(P(), buf[P()]);
+  });
+  for (int k0 = 0; k0 < n_w; k0 += kDepth) {
+    static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+      const int k = k0 + P();
+      if (k < n_w) {
+        compute_tile(k, buf[P()]);
+        if (k + kDepth < n_w) load_tile(k + kDepth, buf[P()]);
+      }
+    });
+  }
+
+  // ---- merge the four wave states through LDS ---------------------------------------------------
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __shared__ float sm_o[kWaves][G][D];
+  if constexpr (MFMA) {
+    float lt = l_run + lane_xor(l_run, 16);
+    lt += lane_xor(lt, 32);
+    if (q4 == 0 && r16 < G) {
+      sm_m[wave][r16] = m_run;
+      sm_l[wave][r16] = lt;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float lt = l_v[j] + lane_xor(l_v[j], 16);
+      lt += lane_xor(lt, 32);
+      if (lane == 0) {
+        sm_m[wave][j] = m_v[j];
+        sm_l[wave][j] = lt;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float o = O[j][e] + lane_xor(O[j][e], 16);
+      o += lane_xor(o, 32);
+      if (q4 == 0) sm_o[wave][j][r16 * EPL + e] = o;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kSplitThreads) {
+    const int j = idx / D;
+    const int e = idx % D;
+    if (j >= g) continue;
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_m[w][j];
+      const float ww = (mw == neg_inf()) ? 0.f : exp2_fast(mw - M);  // empty wave: weight 0
+      L = fmaf(ww, sm_l[w][j], L);
+      acc = fmaf(ww, sm_o[w][j][e], acc);
+    }
+    const int64_t row = q_row0 + j;
+    if (S == 1) {
+      a.out[row * D + e] = acc / L;
+    } else {
+      const int64_t slot = row * S + split;
+      a.o_part[slot * D + e] = acc;
+      if (e == 0) {
+        a.ml_part[slot * 2 + 0] = M;
+        a.ml_part[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Second pass: one wave per (sequence, query head) row merges that row's split states.
+template <int D>
+__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void merge_kernel(const MergeArgs a) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int S = a.num_splits;
+  int nv = S;
+  if (a.num_valid != nullptr) {
+    nv = a.num_valid[row];
+  } else if (a.ctx_lens != nullptr) {
+    int ctx = a.ctx_lens[row / a.h_q];
+    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+    nv = (ctx + a.split_len - 1) / a.split_len;
+  }
+  nv = nv < 0 ? 0 : (nv > S ? S : nv);
+  const float* ml = a.ml_part + int64_t(row) * S * 2;
+  const float* o = a.o_part + int64_t(row) * S * D;
+
+  float M = neg_inf();
+  for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) M = fmaxf(M, lane_xor(M, mask));
+
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float L = 0.f;
+  if (M != neg_inf()) {
+    for (int s = 0; s < nv; ++s) {
+      const float m = ml[2 * s];
+      const float w = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
+      L = fmaf(w, ml[2 * s + 1], L);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[int64_t(s) * D + lane + 64 * e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    a.out[int64_t(row) * D + lane + 64 * e] = L > 0.f ? acc[e] / L : 0.f;
+}
+
+template <int D, int G, bool QB, bool KB, bool MF, int PG>
+int launch_one(const SplitArgs& a, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG>), dim3(uint32_t(grid)), dim3(kSplitThreads),
+                     0, stream, a);
+  return int(hipGetLastError());
+}
+
+template <int D, int G>
+int launch_dtype(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16, bool kv_bf16,
+                 hipStream_t s) {
+  if (plan.variant == 1) {
+    return paged ? launch_one<D, G, true, true, true, 1>(a, plan.grid_split, s)
+                 : launch_one<D, G, true, true, true, 0>(a, plan.grid_split, s);
+  }
+  if (q_bf16 && kv_bf16) return launch_one<D, G, true, true, false, 2>(a, plan.grid_split, s);
+  if (q_bf16) return launch_one<D, G, true, false, false, 2>(a, plan.grid_split, s);
+  if (kv_bf16) return launch_one<D, G, false, true, false, 2>(a, plan.grid_split, s);
+  return launch_one<D, G, false, false, false, 2>(a, plan.grid_split, s);
+}
+
+template <int D>
+int launch_group(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16, bool kv_bf16,
+                 hipStream_t s) {
+  switch (plan.group_padded) {
+    case 1: return launch_dtype<D, 1>(a, plan, paged, q_bf16, kv_bf16, s);
+    case 2: return launch_dtype<D, 2>(a, plan, paged, q_bf16, kv_bf16, s);
+    case 4: return launch_dtype<D, 4>(a, plan, paged, q_bf16, kv_bf16, s);
+    case 8: return launch_dtype<D, 8>(a, plan, paged, q_bf16, kv_bf16, s);
+    case 16: return launch_dtype<D, 16>(a, plan, paged, q_bf16, kv_bf16, s);
+    default: return int(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace
+
+int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, bool q_bf16,
+                 bool kv_bf16, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (head_dim == 64) return launch_group<64>(a, plan, paged, q_bf16, kv_bf16, s);
+  if (head_dim == 128) return launch_group<128>(a, plan, paged, q_bf16, kv_bf16, s);
+  return int(hipErrorInvalidValue);
+}
+
+int launch_merge(const MergeArgs& a, int head_dim, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t grid = uint32_t((int64_t(a.rows) + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(64 * kMergeRowsPerBlock), 0, s, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(64 * kMergeRowsPerBlock), 0, s, a);
+  else
+    return int(hipErrorInvalidValue);
+  return int(hipGetLastError());
+}
+
+}  // namespace kvattn

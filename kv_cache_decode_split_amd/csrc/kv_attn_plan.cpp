@@ -1,0 +1,160 @@
+// Host-only part of the library: argument validation, split planning, the host-side table
+// validator and status strings. No HIP calls, so it builds and runs on a machine without a GPU.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "kv_attn_internal.h"
+
+namespace kvattn {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == KV_ATTN_BF16 ? 2 : 4; }
+
+}  // namespace
+
+int32_t padded_group(int32_t g) {
+  int32_t G = 1;
+  while (G < g) G <<= 1;
+  return G;
+}
+
+bool fault_injected(const char* where) {
+  const char* f = getenv("KV_ATTN_FAULT");
+  return f != nullptr && strcmp(f, where) == 0;
+}
+
+kv_attn_status validate_params(const kv_attn_params* p) {
+  if (p == nullptr) return KV_ATTN_ERR_NULL;
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1) return KV_ATTN_ERR_SHAPE;
+  if (p->num_q_heads % p->num_kv_heads != 0) return KV_ATTN_ERR_SHAPE;
+  const int32_t g = p->num_q_heads / p->num_kv_heads;
+  if (g > 16) return KV_ATTN_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return KV_ATTN_ERR_UNSUPPORTED;
+  if ((p->q_dtype != KV_ATTN_F32 && p->q_dtype != KV_ATTN_BF16) ||
+      (p->kv_dtype != KV_ATTN_F32 && p->kv_dtype != KV_ATTN_BF16))
+    return KV_ATTN_ERR_UNSUPPORTED;
+  if (p->reserved != 0) return KV_ATTN_ERR_VALUE;
+  if (p->max_ctx_len < 0 || p->num_splits < 0) return KV_ATTN_ERR_VALUE;
+  if (!isfinite(p->scale)) return KV_ATTN_ERR_VALUE;
+  if (p->block_size < 1 || p->num_blocks < 1) return KV_ATTN_ERR_SHAPE;
+  const int64_t strides[6] = {p->k_stride_block, p->k_stride_token, p->k_stride_head,
+                              p->v_stride_block, p->v_stride_token, p->v_stride_head};
+  const int eb = elem_bytes(p->kv_dtype);
+  for (int64_t s : strides) {
+    if (s < 0) return KV_ATTN_ERR_SHAPE;
+    // Every row starts 16-byte aligned so that each lane issues whole 128-bit loads.
+    if ((s * eb) % 16 != 0) return KV_ATTN_ERR_UNSUPPORTED;
+  }
+  return KV_ATTN_OK;
+}
+
+kv_attn_status validate_layout(const kv_attn_params* p, bool paged) {
+  const kv_attn_status st = validate_params(p);
+  if (st != KV_ATTN_OK) return st;
+  if (paged) {
+    // Tiles of kTile positions must never straddle two blocks.
+    if (!is_pow2(p->block_size) || p->block_size < kTile) return KV_ATTN_ERR_SHAPE;
+    if (p->max_blocks_per_seq < 1) return KV_ATTN_ERR_SHAPE;
+    if (int64_t(p->max_ctx_len) > int64_t(p->max_blocks_per_seq) * p->block_size)
+      return KV_ATTN_ERR_SHAPE;
+  } else {
+    if (p->max_ctx_len > p->block_size) return KV_ATTN_ERR_SHAPE;
+    if (p->num_blocks < p->batch) return KV_ATTN_ERR_SHAPE;
+  }
+  return KV_ATTN_OK;
+}
+
+// Split planning. The positions of one (sequence, KV head) pair are cut into tiles of kTile,
+// and the tiles into S splits of split_tiles tiles; every split is one workgroup of kWaves
+// waves. The grid is sized from the host-known max_ctx_len: workgroups whose split starts past
+// their own sequence's length exit at once, so ragged batches need no host copy of ctx_lens.
+kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
+  const kv_attn_status st = validate_params(p);
+  if (st != KV_ATTN_OK) return st;
+  if (num_cus < 1) return KV_ATTN_ERR_VALUE;
+  const int64_t tiles_max = ceil_div(p->max_ctx_len > 0 ? p->max_ctx_len : 1, kTile);
+  const int64_t units = int64_t(p->batch) * p->num_kv_heads;
+  int64_t S;
+  if (p->num_splits > 0) {
+    S = p->num_splits;
+  } else {
+    S = ceil_div(int64_t(num_cus) * kWorkgroupsPerCu, units);
+    const int64_t most = ceil_div(tiles_max, kMinSplitTiles);   // splits of >= 16 tiles
+    const int64_t least = ceil_div(tiles_max, kMaxSplitTiles);  // splits of <= 256 tiles
+    if (S > most) S = most;
+    if (S < least) S = least;
+  }
+  if (S > tiles_max) S = tiles_max;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  const int64_t split_tiles = ceil_div(tiles_max, S);
+  S = ceil_div(tiles_max, split_tiles);
+
+  plan->num_splits = int32_t(S);
+  plan->split_tiles = int32_t(split_tiles);
+  plan->group_padded = padded_group(p->num_q_heads / p->num_kv_heads);
+  const bool force_vector = getenv("KV_ATTN_FORCE_VECTOR") != nullptr &&
+                            strcmp(getenv("KV_ATTN_FORCE_VECTOR"), "1") == 0;
+  plan->variant = (p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector) ? 1 : 0;
+  plan->grid_split = units * S;
+  const int64_t rows = int64_t(p->batch) * p->num_q_heads;
+  plan->grid_merge = S > 1 ? ceil_div(rows, kMergeRowsPerBlock) : 0;
+  if (S > 1) {
+    const uint64_t o_bytes = uint64_t(rows) * uint64_t(S) * uint64_t(p->head_dim) * 4u;
+    const uint64_t o_aligned = (o_bytes + 255u) & ~uint64_t(255u);
+    plan->o_part_bytes = o_aligned;
+    plan->workspace_bytes = o_aligned + uint64_t(rows) * uint64_t(S) * 2u * 4u;
+  } else {
+    plan->o_part_bytes = 0;
+    plan->workspace_bytes = 0;
+  }
+  if (plan->grid_split > 0x7fffffffLL || plan->grid_merge > 0x7fffffffLL) return KV_ATTN_ERR_SHAPE;
+  return KV_ATTN_OK;
+}
+
+}  // namespace kvattn
+
+extern "C" {
+
+int32_t kv_attn_abi_version(void) { return KV_ATTN_ABI_VERSION; }
+
+const char* kv_attn_status_string(int32_t status) {
+  switch (status) {
+    case KV_ATTN_OK: return "ok";
+    case KV_ATTN_ERR_NULL: return "a required pointer is NULL";
+    case KV_ATTN_ERR_SHAPE: return "inconsistent sizes";
+    case KV_ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, group size, dtype or alignment";
+    case KV_ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_ATTN_ERR_HIP: return "HIP runtime error";
+    case KV_ATTN_ERR_TABLE: return "ctx_lens or block_table content out of range";
+    case KV_ATTN_ERR_VALUE: return "invalid scalar argument";
+    default: return "unknown status";
+  }
+}
+
+kv_attn_status kv_attn_validate_host(const int32_t* block_table, const int32_t* ctx_lens,
+                                     const kv_attn_params* p) {
+  const bool paged = block_table != nullptr;
+  const kv_attn_status st = kvattn::validate_layout(p, paged);
+  if (st != KV_ATTN_OK) return st;
+  if (ctx_lens == nullptr) return KV_ATTN_ERR_NULL;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    const int32_t len = ctx_lens[b];
+    if (len < 0 || len > p->max_ctx_len) return KV_ATTN_ERR_TABLE;
+    if (!paged) continue;
+    const int64_t nblk = kvattn::ceil_div(len, p->block_size);
+    if (nblk > p->max_blocks_per_seq) return KV_ATTN_ERR_TABLE;
+    const int32_t* row = block_table + int64_t(b) * p->max_blocks_per_seq;
+    for (int64_t i = 0; i < nblk; ++i)
+      if (row[i] < 0 || row[i] >= p->num_blocks) return KV_ATTN_ERR_TABLE;
+  }
+  return KV_ATTN_OK;
+}
+
+}  // extern "C"

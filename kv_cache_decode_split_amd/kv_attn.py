@@ -1,0 +1,348 @@
+"""ctypes binding of ``libkvattn.so`` with the same names as ``include/kv_attn.h``.
+
+Argument marshalling only: tensors are checked against the sizes the call implies (so that no
+launch can address memory outside them), turned into raw device pointers, strides and sizes,
+and handed to the C library together with torch's current HIP stream. Every step of the
+attention runs in the library's HIP kernels; there is no fallback. Importing this module loads
+the library and raises ImportError if it has not been built
+(``python -m kv_cache_decode_split_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "KvAttnError",
+    "kv_attn_params",
+    "kv_attn_plan",
+    "make_params",
+    "kv_attn_abi_version",
+    "kv_attn_status_string",
+    "kv_attn_get_plan",
+    "kv_attn_workspace_size",
+    "kv_attn_decode",
+    "kv_attn_decode_split",
+    "kv_attn_decode_merge",
+    "kv_attn_decode_workload",
+    "DecodeCall",
+    "decode_call_for",
+    "kv_attn_merge",
+    "kv_attn_validate_host",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvattn.so")
+
+KV_ATTN_OK = 0
+KV_ATTN_ERR_NULL = 1
+KV_ATTN_ERR_SHAPE = 2
+KV_ATTN_ERR_UNSUPPORTED = 3
+KV_ATTN_ERR_WORKSPACE = 4
+KV_ATTN_ERR_HIP = 5
+KV_ATTN_ERR_TABLE = 6
+KV_ATTN_ERR_VALUE = 7
+
+KV_ATTN_F32 = 0
+KV_ATTN_BF16 = 1
+
+EXPORTED_SYMBOLS = (
+    "kv_attn_abi_version",
+    "kv_attn_status_string",
+    "kv_attn_get_plan",
+    "kv_attn_workspace_size",
+    "kv_attn_decode",
+    "kv_attn_decode_split",
+    "kv_attn_decode_merge",
+    "kv_attn_merge",
+    "kv_attn_validate_host",
+)
+
+
+class KvAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__(f"{where}: {kv_attn_status_string(status)} (status {status})")
+
+
+class kv_attn_params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("k_stride_block", ctypes.c_int64),
+        ("k_stride_token", ctypes.c_int64),
+        ("k_stride_head", ctypes.c_int64),
+        ("v_stride_block", ctypes.c_int64),
+        ("v_stride_token", ctypes.c_int64),
+        ("v_stride_head", ctypes.c_int64),
+    ]
+
+
+class kv_attn_plan(ctypes.Structure):
+    _fields_ = [
+        ("num_splits", ctypes.c_int32),
+        ("split_len", ctypes.c_int32),
+        ("grid_split", ctypes.c_int32),
+        ("grid_merge", ctypes.c_int32),
+        ("kernel_variant", ctypes.c_int32),
+        ("group_padded", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("ml_offset", ctypes.c_uint64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m kv_cache_decode_split_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.kv_attn_abi_version.argtypes = []
+    lib.kv_attn_abi_version.restype = ctypes.c_int32
+    lib.kv_attn_status_string.argtypes = [ctypes.c_int32]
+    lib.kv_attn_status_string.restype = ctypes.c_char_p
+    lib.kv_attn_get_plan.argtypes = [P(kv_attn_params), ctypes.c_int32, P(kv_attn_plan)]
+    lib.kv_attn_get_plan.restype = ctypes.c_int
+    lib.kv_attn_workspace_size.argtypes = [P(kv_attn_params)]
+    lib.kv_attn_workspace_size.restype = ctypes.c_size_t
+    lib.kv_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, P(kv_attn_params), vp, ctypes.c_size_t, vp]
+    lib.kv_attn_decode.restype = ctypes.c_int
+    lib.kv_attn_decode_split.argtypes = [vp, vp, vp, vp, vp, vp, P(kv_attn_params), vp, ctypes.c_size_t, vp]
+    lib.kv_attn_decode_split.restype = ctypes.c_int
+    lib.kv_attn_decode_merge.argtypes = [vp, vp, P(kv_attn_params), vp, ctypes.c_size_t, vp]
+    lib.kv_attn_decode_merge.restype = ctypes.c_int
+    lib.kv_attn_merge.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.kv_attn_merge.restype = ctypes.c_int
+    lib.kv_attn_validate_host.argtypes = [vp, vp, P(kv_attn_params)]
+    lib.kv_attn_validate_host.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def kv_attn_abi_version() -> int:
+    return int(_lib.kv_attn_abi_version())
+
+
+def kv_attn_status_string(status: int) -> str:
+    return _lib.kv_attn_status_string(int(status)).decode()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KV_ATTN_BF16
+    if dt == torch.float32:
+        return KV_ATTN_F32
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
+
+
+def make_params(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, max_ctx_len: int, num_blocks: int,
+                k_strides: Sequence[int], v_strides: Sequence[int],
+                max_blocks_per_seq: int = 1, num_splits: int = 0,
+                q_dtype: int = KV_ATTN_BF16, kv_dtype: int = KV_ATTN_BF16,
+                scale: float = 0.0) -> kv_attn_params:
+    """Fill a ``kv_attn_params`` (strides are (block, token, head) in elements)."""
+    p = kv_attn_params()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = batch, num_q_heads, num_kv_heads, head_dim
+    p.block_size, p.max_blocks_per_seq, p.max_ctx_len = block_size, max_blocks_per_seq, max_ctx_len
+    p.num_splits, p.q_dtype, p.kv_dtype, p.scale, p.reserved = num_splits, q_dtype, kv_dtype, scale, 0
+    p.num_blocks = num_blocks
+    p.k_stride_block, p.k_stride_token, p.k_stride_head = (int(s) for s in k_strides)
+    p.v_stride_block, p.v_stride_token, p.v_stride_head = (int(s) for s in v_strides)
+    return p
+
+
+def kv_attn_get_plan(params: kv_attn_params, num_cus: int = 0) -> dict:
+    plan = kv_attn_plan()
+    st = _lib.kv_attn_get_plan(ctypes.byref(params), int(num_cus), ctypes.byref(plan))
+    if st != KV_ATTN_OK:
+        raise KvAttnError(st, "kv_attn_get_plan")
+    return {name: getattr(plan, name) for name, _ in kv_attn_plan._fields_ if name != "reserved"}
+
+
+def kv_attn_workspace_size(params: kv_attn_params) -> int:
+    return int(_lib.kv_attn_workspace_size(ctypes.byref(params)))
+
+
+def kv_attn_validate_host(block_table, ctx_lens, params: kv_attn_params) -> int:
+    """Host-side content check; ``block_table``/``ctx_lens`` are CPU int32 tensors (or None)."""
+    ctx = ctx_lens.detach().to("cpu", torch.int32).contiguous()
+    bt = None if block_table is None else block_table.detach().to("cpu", torch.int32).contiguous()
+    return int(_lib.kv_attn_validate_host(None if bt is None else bt.data_ptr(), ctx.data_ptr(),
+                                          ctypes.byref(params)))
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _check_extent(t: torch.Tensor, strides, blocks: int, slots: int, heads: int, d: int, what: str):
+    last = (blocks - 1) * strides[0] + (slots - 1) * strides[1] + (heads - 1) * strides[2] + d - 1
+    avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if last >= avail:
+        raise ValueError(f"{what}: strides address element {last} but only {avail} exist")
+
+
+class DecodeCall:
+    """Checked, marshalled arguments of one decode problem (reusable across launches).
+
+    q: [B, h_q, d] contiguous bf16/fp32; out: [B, h_q, d] contiguous fp32. k_cache/v_cache:
+    device tensors of one dtype holding num_kv_heads heads, whose element (block, token, head, i)
+    is at block*strides[0] + token*strides[1] + head*strides[2] + i. block_table: int32
+    [B, max_blocks] (paged; block_size tokens per block) or None (contiguous; block_size = slot
+    capacity). ctx_lens: int32 [B] on the device. max_ctx_len defaults to ctx_lens.max() (a host
+    sync). The workspace, if not given, is allocated once from torch's allocator.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, ctx_lens, out, *, num_kv_heads: int,
+                 k_strides: Sequence[int], v_strides: Sequence[int], block_size: int,
+                 num_blocks: int, max_ctx_len: Optional[int] = None, scale: float = 0.0,
+                 num_splits: int = 0, workspace: Optional[torch.Tensor] = None):
+        if q.dim() != 3 or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, h_q, d] tensor")
+        B, hq, d = q.shape
+        if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous fp32 tensor shaped like q")
+        if k_cache.dtype != v_cache.dtype:
+            raise ValueError("k_cache and v_cache must share a dtype")
+        dev = q.device
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens),
+                        ("out", out)):
+            if t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, q on {dev}")
+        if ctx_lens.dtype != torch.int32 or ctx_lens.shape != (B,) or not ctx_lens.is_contiguous():
+            raise ValueError("ctx_lens must be a contiguous int32 [B] tensor")
+        if block_table is not None:
+            if (block_table.dtype != torch.int32 or block_table.dim() != 2
+                    or block_table.shape[0] != B or not block_table.is_contiguous()
+                    or block_table.device != dev):
+                raise ValueError("block_table must be a contiguous int32 [B, max_blocks] device tensor")
+            max_blocks = int(block_table.shape[1])
+        else:
+            max_blocks = 1
+        if max_ctx_len is None:
+            max_ctx_len = int(ctx_lens.max().item()) if B else 0
+        hkv = int(num_kv_heads)
+        self.params = make_params(
+            batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=block_size,
+            max_ctx_len=int(max_ctx_len), num_blocks=num_blocks, k_strides=k_strides,
+            v_strides=v_strides, max_blocks_per_seq=max_blocks, num_splits=num_splits,
+            q_dtype=_dtype_code(q.dtype), kv_dtype=_dtype_code(k_cache.dtype), scale=float(scale))
+        _check_extent(k_cache, k_strides, num_blocks, block_size, hkv, d, "k_cache")
+        _check_extent(v_cache, v_strides, num_blocks, block_size, hkv, d, "v_cache")
+        ws_bytes = kv_attn_workspace_size(self.params)
+        if ws_bytes and workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        if workspace is not None and workspace.device != dev:
+            raise ValueError("workspace must be on q's device")
+        self.workspace = workspace
+        self._keep = (q, k_cache, v_cache, block_table, ctx_lens, out)
+        self._ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                      None if block_table is None else block_table.data_ptr(),
+                      ctx_lens.data_ptr(), out.data_ptr())
+        self._ws = (workspace.data_ptr() if workspace is not None else None,
+                    workspace.numel() * workspace.element_size() if workspace is not None else 0)
+
+    def plan(self) -> dict:
+        return kv_attn_get_plan(self.params)
+
+    def decode(self, stream=None) -> None:
+        st = _lib.kv_attn_decode(*self._ptrs, ctypes.byref(self.params), *self._ws,
+                                 _stream_handle(stream))
+        if st != KV_ATTN_OK:
+            raise KvAttnError(st, "kv_attn_decode")
+
+    def split(self, stream=None) -> None:
+        st = _lib.kv_attn_decode_split(*self._ptrs, ctypes.byref(self.params), *self._ws,
+                                       _stream_handle(stream))
+        if st != KV_ATTN_OK:
+            raise KvAttnError(st, "kv_attn_decode_split")
+
+    def merge(self, stream=None) -> None:
+        st = _lib.kv_attn_decode_merge(self._ptrs[4], self._ptrs[5], ctypes.byref(self.params),
+                                       *self._ws, _stream_handle(stream))
+        if st != KV_ATTN_OK:
+            raise KvAttnError(st, "kv_attn_decode_merge")
+
+
+def kv_attn_decode(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None, **kwargs) -> None:
+    """Enqueue one decode-attention step (both passes); arguments as for :class:`DecodeCall`."""
+    DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, **kwargs).decode(stream)
+
+
+def kv_attn_decode_split(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None,
+                         **kwargs) -> DecodeCall:
+    """Enqueue the streaming pass only; returns the call (its workspace holds the split states)."""
+    call = DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, **kwargs)
+    call.split(stream)
+    return call
+
+
+def kv_attn_decode_merge(call: DecodeCall, stream=None) -> None:
+    """Enqueue the merge pass over the workspace of a :func:`kv_attn_decode_split` call."""
+    call.merge(stream)
+
+
+def _workload_args(w) -> dict:
+    ks, vs = w.kv_strides()
+    return dict(num_kv_heads=w.spec.num_kv_heads, k_strides=ks, v_strides=vs,
+                block_size=w.block_size, num_blocks=w.num_blocks, max_ctx_len=w.max_ctx_len)
+
+
+def kv_attn_decode_workload(w, out: torch.Tensor, *, stream=None, **kwargs) -> None:
+    """kv_attn_decode on a workload object (attributes q, k_cache, v_cache, block_table, ctx_lens,
+    block_size, num_blocks, max_ctx_len, spec.num_kv_heads and kv_strides()), e.g. one built by
+    ``kv_cache_decode_split_amd.workloads.make_workload``."""
+    args = _workload_args(w)
+    args.update(kwargs)
+    kv_attn_decode(w.q, w.k_cache, w.v_cache, w.block_table, w.ctx_lens, out, stream=stream, **args)
+
+
+def decode_call_for(w, out: torch.Tensor, **kwargs) -> DecodeCall:
+    """A reusable :class:`DecodeCall` for a workload object."""
+    args = _workload_args(w)
+    args.update(kwargs)
+    return DecodeCall(w.q, w.k_cache, w.v_cache, w.block_table, w.ctx_lens, out, **args)
+
+
+def kv_attn_merge(o_partial: torch.Tensor, ml_partial: torch.Tensor,
+                  num_valid: Optional[torch.Tensor], out: torch.Tensor, stream=None) -> None:
+    """Merge split states: o_partial [rows, S, d], ml_partial [rows, S, 2] (base-2 maxima, sums),
+    num_valid int32 [rows] or None, out [rows, d] fp32. All contiguous fp32 on one device."""
+    if o_partial.dim() != 3 or ml_partial.dim() != 3:
+        raise ValueError("o_partial must be [rows, S, d] and ml_partial [rows, S, 2]")
+    rows, S, d = o_partial.shape
+    if ml_partial.shape != (rows, S, 2) or out.shape != (rows, d):
+        raise ValueError("shape mismatch between o_partial, ml_partial and out")
+    for t in (o_partial, ml_partial, out):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != o_partial.device:
+            raise ValueError("merge tensors must be contiguous fp32 on one device")
+    if num_valid is not None and (num_valid.dtype != torch.int32 or num_valid.shape != (rows,)
+                                  or not num_valid.is_contiguous()):
+        raise ValueError("num_valid must be a contiguous int32 [rows] tensor")
+    st = _lib.kv_attn_merge(o_partial.data_ptr(), ml_partial.data_ptr(),
+                            None if num_valid is None else num_valid.data_ptr(), out.data_ptr(),
+                            rows, S, d, _stream_handle(stream))
+    if st != KV_ATTN_OK:
+        raise KvAttnError(st, "kv_attn_merge")

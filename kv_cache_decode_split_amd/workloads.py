@@ -293,15 +293,22 @@ def oracle_view(w: Workload) -> dict:
     )
 
 
-def oracle_sample(w: Workload, seqs) -> dict:
-    """Host copy of only the sequences ``seqs``, in the oracle's conventions.
+def oracle_sample(w: Workload, seqs, kv_heads=None) -> dict:
+    """Host copy of only the sequences ``seqs`` (and optionally only the KV heads ``kv_heads``
+    with their query heads), in the oracle's conventions.
 
     The physical blocks a sampled sequence uses are copied (nothing else), and the block table
-    is renumbered to the copy. Output rows of the oracle correspond to ``seqs`` in order.
+    is renumbered to the copy. Oracle output rows correspond to ``seqs`` in order, and its head
+    axis to the query heads of ``kv_heads`` in order.
     """
     seqs = [int(s) for s in seqs]
     ctx = w.ctx_lens.cpu().to(torch.int64)
-    q = _np_storage(w.q[seqs])
+    q_sel = w.q[seqs]
+    if kv_heads is not None:
+        g = w.spec.group
+        heads = [kvh * g + j for kvh in kv_heads for j in range(g)]
+        q_sel = q_sel[:, heads]
+    q = _np_storage(q_sel)
     if w.block_table is None:
         idx = torch.tensor(seqs, dtype=torch.int64, device=w.k_cache.device)
         k = w.k_cache.index_select(0, idx)
@@ -322,6 +329,12 @@ def oracle_sample(w: Workload, seqs) -> dict:
         table = np.zeros((len(seqs), width), dtype=np.int64)
         for i, r in enumerate(rows):
             table[i, :len(r)] = r
+
+    if kv_heads is not None:
+        axis = 1 if w.spec.layout == "head_major" else 2
+        hidx = torch.tensor([int(h) for h in kv_heads], dtype=torch.int64, device=k.device)
+        k = k.index_select(axis, hidx)
+        v = v.index_select(axis, hidx)
 
     def bshd(t):
         a = _np_storage(t)

@@ -1,0 +1,210 @@
+"""C-ABI checks that need no GPU: exports, struct layout, planning and host-side error paths.
+
+Every call here fails validation (or is a pure host function) before the library makes any HIP
+call, so nothing touches a device.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kv_attn.h")
+
+K = pytest.importorskip("kv_cache_decode_split_amd.kv_attn",
+                        reason="libkvattn.so not built (run python -m kv_cache_decode_split_amd.build)")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_attn_\w+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported():
+    declared = _declared_functions()
+    assert declared == sorted(K.EXPORTED_SYMBOLS)
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (kv_attn_\w+)", out.stdout))
+    assert exported == set(declared)
+
+
+def test_struct_layout_matches_the_header():
+    """Compile a probe against the header and compare every offset with the ctypes mirror."""
+    fields = {"kv_attn_params": K.kv_attn_params, "kv_attn_plan": K.kv_attn_plan}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "kv_attn.h"', "int main(void){"]
+    for sname, cls in fields.items():
+        lines.append(f'printf("{sname} size %zu\\n", sizeof({sname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'printf("{sname} {fname} %zu\\n", offsetof({sname}, {fname}));')
+    lines.append("return 0;}")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "probe.c"), os.path.join(d, "probe")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    for line in out.splitlines():
+        sname, what, value = line.split()
+        cls = fields[sname]
+        if what == "size":
+            assert ctypes.sizeof(cls) == int(value), sname
+        else:
+            assert getattr(cls, what).offset == int(value), (sname, what)
+
+
+def test_abi_version_and_status_strings():
+    assert K.kv_attn_abi_version() == 1
+    for code in range(8):
+        s = K.kv_attn_status_string(code)
+        assert s and s != "unknown status"
+    assert K.kv_attn_status_string(99) == "unknown status"
+
+
+def _params(**kw):
+    base = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                max_ctx_len=1000, num_blocks=300, k_strides=(8 * 16 * 128, 128, 16 * 128),
+                v_strides=(8 * 16 * 128, 128, 16 * 128), max_blocks_per_seq=63)
+    base.update(kw)
+    return K.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), K.KV_ATTN_ERR_SHAPE),
+    (dict(num_q_heads=30), K.KV_ATTN_ERR_SHAPE),            # not a multiple of h_kv
+    (dict(num_q_heads=8 * 17), K.KV_ATTN_ERR_UNSUPPORTED),  # group 17 > 16
+    (dict(head_dim=96), K.KV_ATTN_ERR_UNSUPPORTED),
+    (dict(q_dtype=5), K.KV_ATTN_ERR_UNSUPPORTED),
+    (dict(k_strides=(8 * 16 * 128, 127, 16 * 128)), K.KV_ATTN_ERR_UNSUPPORTED),  # misaligned rows
+    (dict(v_strides=(-1, 128, 16 * 128)), K.KV_ATTN_ERR_SHAPE),
+    (dict(max_ctx_len=-1), K.KV_ATTN_ERR_VALUE),
+    (dict(num_splits=-2), K.KV_ATTN_ERR_VALUE),
+    (dict(scale=float("nan")), K.KV_ATTN_ERR_VALUE),
+    (dict(num_blocks=0), K.KV_ATTN_ERR_SHAPE),
+])
+def test_get_plan_rejects_invalid_params(kw, status):
+    p = _params(**kw)
+    with pytest.raises(K.KvAttnError) as e:
+        K.kv_attn_get_plan(p, 256)
+    assert e.value.status == status
+
+
+def test_plan_covers_every_tile_and_respects_bounds():
+    for B, hkv, T in [(1, 8, 256), (8, 32, 4096), (64, 8, 8192), (128, 8, 32768), (4, 8, 131072),
+                      (3, 2, 1), (2, 1, 17), (1, 1, 5000)]:
+        for cus in (1, 80, 256, 304):
+            p = _params(batch=B, num_q_heads=hkv * 2, num_kv_heads=hkv, max_ctx_len=T,
+                        block_size=16, max_blocks_per_seq=(T + 15) // 16, num_blocks=10**6)
+            plan = K.kv_attn_get_plan(p, cus)
+            tiles = (T + 15) // 16
+            S, L = plan["num_splits"], plan["split_len"]
+            assert L % 16 == 0 and S >= 1
+            assert S * L >= T and (S - 1) * L < T          # every position in exactly one split
+            assert plan["grid_split"] == B * hkv * S
+            if S > 1:
+                assert L // 16 >= min(16, tiles)             # splits of >= 16 tiles when possible
+                assert plan["workspace_bytes"] >= B * hkv * 2 * S * (128 + 2) * 4
+                assert plan["grid_merge"] == (B * hkv * 2 + 3) // 4
+            else:
+                assert plan["workspace_bytes"] == 0 and plan["grid_merge"] == 0
+            assert L // 16 <= 256 or S == 4096
+
+
+def test_plan_for_the_five_workloads():
+    """Launch geometry of C1-C5 on a 256-CU device (what the bench times)."""
+    want = {  # (B, h_q, h_kv, T) -> (S, split_len)
+        (1, 8, 8, 256): (1, 256),
+        (8, 32, 32, 4096): (8, 512),
+        (64, 32, 8, 8192): (4, 2048),
+        (128, 32, 8, 32768): (8, 4096),
+        (4, 64, 8, 131072): (64, 2048),
+    }
+    for (B, hq, hkv, T), (S, L) in want.items():
+        p = _params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
+                    max_blocks_per_seq=(T + 15) // 16, num_blocks=10**6)
+        plan = K.kv_attn_get_plan(p, 256)
+        assert (plan["num_splits"], plan["split_len"]) == (S, L)
+        assert plan["kernel_variant"] == 1
+
+
+def test_explicit_split_count_and_variant_selection():
+    p = _params(num_splits=3)
+    plan = K.kv_attn_get_plan(p, 256)
+    assert plan["num_splits"] == 3 and plan["split_len"] == 336
+    p = _params(q_dtype=K.KV_ATTN_F32)
+    assert K.kv_attn_get_plan(p, 256)["kernel_variant"] == 0
+    p = _params(num_q_heads=8 * 3)
+    assert K.kv_attn_get_plan(p, 256)["group_padded"] == 4
+
+
+def _decode_raw(p, q=16, k=16, v=16, bt=16, ctx=16, out=16, ws=None, ws_bytes=0):
+    lib = K._lib
+    return lib.kv_attn_decode(q, k, v, bt, ctx, out, ctypes.byref(p), ws, ws_bytes, None)
+
+
+def test_decode_null_pointers_fail_before_any_hip_call():
+    p = _params()
+    assert _decode_raw(p, q=None) == K.KV_ATTN_ERR_NULL
+    assert _decode_raw(p, ctx=None) == K.KV_ATTN_ERR_NULL
+    assert _decode_raw(p, out=None) == K.KV_ATTN_ERR_NULL
+    assert K._lib.kv_attn_decode(16, 16, 16, 16, 16, 16, None, None, 0, None) == K.KV_ATTN_ERR_NULL
+
+
+def test_decode_layout_errors_fail_before_any_hip_call():
+    assert _decode_raw(_params(block_size=24)) == K.KV_ATTN_ERR_SHAPE            # not a power of 2
+    assert _decode_raw(_params(block_size=8, max_blocks_per_seq=200)) == K.KV_ATTN_ERR_SHAPE
+    assert _decode_raw(_params(max_ctx_len=63 * 16 + 1)) == K.KV_ATTN_ERR_SHAPE  # exceeds the table
+    assert _decode_raw(_params(block_size=500), bt=None) == K.KV_ATTN_ERR_SHAPE  # capacity < max ctx
+    assert _decode_raw(_params(block_size=1000, num_blocks=3), bt=None) == K.KV_ATTN_ERR_SHAPE
+    assert _decode_raw(_params(), q=8) == K.KV_ATTN_ERR_UNSUPPORTED              # misaligned
+    assert _decode_raw(_params(head_dim=32)) == K.KV_ATTN_ERR_UNSUPPORTED
+
+
+def test_simulated_hip_failure(monkeypatch):
+    monkeypatch.setenv("KV_ATTN_FAULT", "query")
+    assert _decode_raw(_params()) == K.KV_ATTN_ERR_HIP
+    plan = K.kv_attn_plan()
+    assert K._lib.kv_attn_get_plan(ctypes.byref(_params()), 0, ctypes.byref(plan)) == K.KV_ATTN_ERR_HIP
+    assert K.kv_attn_workspace_size(_params()) == 0
+
+
+def test_merge_argument_errors():
+    lib = K._lib
+    assert lib.kv_attn_merge(None, 16, None, 16, 4, 2, 128, None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_merge(16, 16, None, 16, 0, 2, 128, None) == K.KV_ATTN_ERR_SHAPE
+    assert lib.kv_attn_merge(16, 16, None, 16, 4, 0, 128, None) == K.KV_ATTN_ERR_SHAPE
+    assert lib.kv_attn_merge(16, 16, None, 16, 4, 2, 100, None) == K.KV_ATTN_ERR_UNSUPPORTED
+
+
+def test_host_validator():
+    p = _params(batch=3, max_ctx_len=40, max_blocks_per_seq=3, num_blocks=10)
+    ctx = torch.tensor([40, 1, 0], dtype=torch.int32)
+    bt = torch.tensor([[0, 1, 2], [9, -5, -5], [-1, -1, -1]], dtype=torch.int32)
+    assert K.kv_attn_validate_host(bt, ctx, p) == K.KV_ATTN_OK
+    bad = bt.clone()
+    bad[0, 2] = 10
+    assert K.kv_attn_validate_host(bad, ctx, p) == K.KV_ATTN_ERR_TABLE
+    bad = bt.clone()
+    bad[1, 0] = -1
+    assert K.kv_attn_validate_host(bad, ctx, p) == K.KV_ATTN_ERR_TABLE
+    assert K.kv_attn_validate_host(bt, torch.tensor([41, 1, 0], dtype=torch.int32), p) == K.KV_ATTN_ERR_TABLE
+    assert K.kv_attn_validate_host(bt, torch.tensor([3, -1, 0], dtype=torch.int32), p) == K.KV_ATTN_ERR_TABLE
+    pc = _params(batch=3, max_ctx_len=40, block_size=40, num_blocks=3)
+    assert K.kv_attn_validate_host(None, ctx, pc) == K.KV_ATTN_OK
+
+
+def test_binding_rejects_tensors_too_small_for_the_strides():
+    q = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    out = torch.zeros(2, 4, 64, dtype=torch.float32)
+    k = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)  # contiguous head major, capacity 8
+    ctx = torch.tensor([8, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        K.kv_attn_decode(q, k, k, None, ctx, out, num_kv_heads=2, k_strides=(2 * 8 * 64, 64, 8 * 64),
+                         v_strides=(2 * 8 * 64, 64, 8 * 64), block_size=9, num_blocks=2, max_ctx_len=8)

@@ -1,0 +1,131 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same inputs.
+
+Small cases span several tiles, several splits and a ragged last tile and are compared element
+by element; the five workloads at full size (in the launch configuration the bench times) are
+compared on sampled (sequence, KV head) rows the oracle computes one by one. Tolerance: max abs
+error <= 5e-3 and max abs error / max |ref| <= 1e-2 on the fp32 output.
+"""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_decode_split_amd import workloads as W
+from tests.gpu_helpers import (announce, check_close, loaded_native_libraries, oracle_full,
+                               oracle_rows, require_gpu, run, select_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_native_library_is_the_one_running():
+    require_gpu()
+    libs = loaded_native_libraries()
+    assert libs and all(p.endswith("kv_cache_decode_split_amd/libkvattn.so") for p in libs), libs
+
+
+SMALL = [
+    ("C1", dict()),
+    ("C1", dict(num_splits=4)),
+    ("C2", dict(batch=2, ctx=(700, 700))),
+    ("C2", dict(batch=2, ctx=(700, 333), capacity=720, layout="token_major")),
+    ("C3", dict(batch=3, ctx=(1000,) * 3)),
+    ("C4", dict(batch=6, ctx=("uniform", 1, 700))),
+    ("C4", dict(batch=5, ctx=("uniform", 1, 300), layout="token_major", extra_blocks=7)),
+    ("C5", dict(batch=2, ctx=(3000, 2999))),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_small_workloads_match_oracle(name, over, num_splits):
+    require_gpu()
+    kw = dict(over)
+    forced = kw.pop("num_splits", None)
+    spec = W.preset(name, **kw)
+    announce(f"small {name} {kw} num_splits={forced or num_splits}")
+    w = W.make_workload(spec, device="cuda")
+    out = run(w, num_splits=forced if forced is not None else num_splits)
+    check_close(out.cpu().numpy(), oracle_full(w), f"{name} {kw} S={num_splits}")
+
+
+def _random_specs(n, seed=7):
+    rnd = random.Random(seed)
+    specs = []
+    for i in range(n):
+        d = rnd.choice([64, 128])
+        g = rnd.choice([1, 2, 3, 4, 5, 8, 16])
+        hkv = rnd.choice([1, 2, 3])
+        B = rnd.randint(1, 4)
+        paged = rnd.random() < 0.5
+        lens = tuple(rnd.randint(1, 2500) for _ in range(B))
+        if rnd.random() < 0.2:
+            lens = tuple(rnd.randint(1, 40) for _ in range(B))
+        qd, kd = rnd.choice([("bf16", "bf16"), ("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16"),
+                             ("bf16", "f32")])
+        specs.append(dict(
+            spec=W.WorkloadSpec(
+                name=f"rand{i}", batch=B, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, ctx=lens,
+                paged=paged, block_size=rnd.choice([16, 32, 64]) if paged else 16, kv_dtype=kd,
+                q_dtype=qd, q_std=rnd.choice([1.0, 2.0, 4.0]), num_sinks=rnd.choice([0, 0, 4]),
+                layout=rnd.choice(["head_major", "token_major"]), seed=5000 + i,
+                extra_blocks=rnd.randint(1, 4),
+                capacity=None if paged else max(lens) + rnd.choice([0, 0, 5])),
+            num_splits=rnd.choice([0, 0, 1, 2, 7])))
+    return specs
+
+
+RANDOM = _random_specs(40)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c["spec"].name for c in RANDOM])
+def test_random_shapes_match_oracle(case):
+    require_gpu()
+    spec = case["spec"]
+    announce(f"random {spec}")
+    w = W.make_workload(spec, device="cuda")
+    out = run(w, num_splits=case["num_splits"])
+    check_close(out.cpu().numpy(), oracle_full(w), spec.name)
+
+
+def test_explicit_scale_matches_oracle():
+    require_gpu()
+    w = W.make_workload(W.preset("C3", batch=2, ctx=(500, 77)), device="cuda")
+    out = run(w, scale=0.05)
+    check_close(out.cpu().numpy(), oracle_full(w, scale=0.05), "scale=0.05")
+
+
+FULL = [
+    ("C1", None, None),
+    ("C2", [0, 7], [0, 13, 31]),
+    ("C3", [0, 63], [0, 7]),
+    ("C4", "extremes", [0, 7]),
+    ("C5", [0, 3], [0, 5]),
+]
+
+
+@pytest.mark.parametrize("name,seqs,heads", FULL, ids=[f[0] for f in FULL])
+def test_full_size_workloads_on_sampled_rows(name, seqs, heads):
+    """The bench's launch configuration (auto split plan) at full size; sampled rows checked.
+
+    C4 samples its shortest, longest and a middle sequence. C2 is one of its 32 layers.
+    """
+    require_gpu()
+    announce(f"full {name}")
+    w = W.make_workload(W.PRESETS[name], device="cuda")
+    try:
+        out = run(w)
+        if seqs is None:
+            check_close(out.cpu().numpy(), oracle_full(w), f"full {name}")
+            return
+        assert torch.isfinite(out).all(), "non-finite output somewhere in the full batch"
+        if seqs == "extremes":
+            ctx = w.ctx_lens.cpu().numpy()
+            order = np.argsort(ctx, kind="stable")
+            seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+        ref = oracle_rows(w, seqs, heads)
+        check_close(select_rows(out, w, seqs, heads), ref, f"full {name} seqs={seqs} heads={heads}")
+    finally:
+        del w
+        torch.cuda.empty_cache()
