@@ -139,6 +139,11 @@ def test_short_sequences_in_a_long_plan_leave_splits_empty():
     """max_ctx_len far above the real lengths: most split workgroups have nothing to do."""
     require_gpu()
     w = W.make_workload(W.preset("C4", batch=5, ctx=(1, 17, 33, 2, 16)), device="cuda")
+    # Widen the table to 2048 columns (entries past each sequence point at the NaN block) so
+    # that a 32768-position plan is valid for it.
+    pad = torch.full((5, 2048 - w.block_table.shape[1]), int(w.block_table[0, -1]),
+                     dtype=torch.int32, device="cuda")
+    w.block_table = torch.cat([w.block_table, pad], dim=1).contiguous()
     out = run(w, max_ctx_len=32768, num_splits=0)
     check_close(out.cpu().numpy(), oracle_full(w), "short in long plan")
 
