@@ -124,7 +124,7 @@ const char* kv_attn_status_string(int32_t status);
  * Plan the launch for `p` as if on a device with `num_cus` compute units (0 = query the
  * current HIP device). Validates `p` exactly as kv_attn_decode does (pointers aside). Split
  * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
- * workgroups number about 8 per compute unit, each split spans 16..256 tiles, and a
+ * workgroups number about 4 per compute unit, each split spans 16..256 tiles, and a
  * caller-given num_splits overrides the count. Writes *plan only on KV_ATTN_OK.
  */
 kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_attn_plan* plan);
@@ -189,7 +189,7 @@ kv_attn_status kv_attn_decode_merge(const int32_t* ctx_lens, float* out, const k
  * num_valid  : device int32 [rows] (only the first num_valid[r] splits of row r are merged,
  *              clamped to [0, num_splits]) or NULL (all splits).
  * out        : device fp32 [rows, head_dim]; a row with no non-empty state is written as zeros.
- * head_dim   : 64 or 128.
+ * head_dim   : 64 or 128; num_splits at most 4096.
  */
 kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
                              const int32_t* num_valid, float* out, int32_t rows,

@@ -227,7 +227,7 @@ kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
   if (o_partial == nullptr || ml_partial == nullptr || out == nullptr) return KV_ATTN_ERR_NULL;
   if (rows < 1 || num_splits < 1) return KV_ATTN_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return KV_ATTN_ERR_UNSUPPORTED;
-  if (int64_t(rows) * num_splits > (int64_t(1) << 40)) return KV_ATTN_ERR_SHAPE;
+  if (num_splits > kvattn::kMaxSplits) return KV_ATTN_ERR_UNSUPPORTED;
   if (kvattn::fault_injected("launch")) return KV_ATTN_ERR_HIP;
   kvattn::MergeArgs m;
   m.o_part = o_partial;

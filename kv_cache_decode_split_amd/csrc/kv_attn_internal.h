@@ -11,14 +11,17 @@ namespace kvattn {
 // Positions per tile: one MFMA row block, and one 16-token block of a paged cache.
 constexpr int kTile = 16;
 // Waves per split workgroup; each wave streams every kWaves-th tile of the split.
-constexpr int kWaves = 4;
+#ifndef KV_ATTN_WAVES
+#define KV_ATTN_WAVES 4
+#endif
+constexpr int kWaves = KV_ATTN_WAVES;
 constexpr int kSplitThreads = 64 * kWaves;
-// Rows (sequence, query head) merged per merge workgroup: one wave each.
-constexpr int kMergeRowsPerBlock = 4;
+// Merge pass: one workgroup of kMergeThreads per (sequence, query head) row.
+constexpr int kMergeThreads = 256;
 // Split planning constants (see make_plan).
 constexpr int kMinSplitTiles = 16;     // a split spans at least 256 positions ...
 constexpr int kMaxSplitTiles = 256;    // ... and at most 4096 positions
-constexpr int kWorkgroupsPerCu = 8;    // target split workgroups per compute unit
+constexpr int kWorkgroupsPerCu = 4;    // target split workgroups per compute unit
 constexpr int kMaxSplits = 4096;
 
 // Everything the split kernel needs, by value.

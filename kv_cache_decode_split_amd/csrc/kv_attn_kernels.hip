@@ -47,7 +47,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kDepth = 2;  // tiles in flight per wave
+#ifndef KV_ATTN_DEPTH
+#define KV_ATTN_DEPTH 2
+#endif
+#ifndef KV_ATTN_NONTEMPORAL
+#define KV_ATTN_NONTEMPORAL 1
+#endif
+constexpr int kDepth = KV_ATTN_DEPTH;  // tiles in flight per wave
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -91,6 +97,35 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 __device__ __forceinline__ float lane_xor(float x, int mask) { return __shfl_xor(x, mask); }
 
+// Combine each lane's value with lane ^ 16 (rows 0<->1, 2<->3) or lane ^ 32 (rows 0<->2,
+// 1<->3) through the gfx950 row-swap permutes; both lanes of a pair compute the same
+// expression in the same operand order, so they end with bit-identical results.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// One 128-bit load of streamed (read-once) cache data.
+__device__ __forceinline__ u32x4_t load_stream16(const char* p) {
+#if KV_ATTN_NONTEMPORAL
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#else
+  return *reinterpret_cast<const u32x4_t*>(p);
+#endif
+}
+
 // Raw per-lane slice of one row: BYTES = 8, 16 or 32.
 template <int BYTES>
 struct Seg {
@@ -106,7 +141,7 @@ __device__ __forceinline__ Seg<BYTES> load_seg(const char* p) {
     s.w[1] = x[1];
   } else {
     static_for<0, BYTES / 16>([&](auto I) __attribute__((always_inline)) {
-      const u32x4_t x = reinterpret_cast<const u32x4_t*>(p)[I()];
+      const u32x4_t x = load_stream16(p + 16 * I());
       s.w[4 * I() + 0] = x[0];
       s.w[4 * I() + 1] = x[1];
       s.w[4 * I() + 2] = x[2];
@@ -149,9 +184,15 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   const int r16 = lane & 15;
   const int q4 = lane >> 4;
 
+  // Workgroups are dealt to the eight XCDs round-robin by index. With the split index slowest,
+  // consecutive indices are different (sequence, KV head) units of the same split, so every
+  // XCD receives the same mix of early (always full) and late (often empty) splits; with the
+  // split index fastest, XCD k would get split k of every unit and ragged batches would load
+  // the XCDs very unevenly.
   const int S = a.num_splits;
-  const int split = blockIdx.x % S;
-  const int unit = blockIdx.x / S;
+  const int units = int(gridDim.x) / S;
+  const int split = blockIdx.x / units;
+  const int unit = blockIdx.x - split * units;
   const int kvh = unit % a.h_kv;
   const int b = unit / a.h_kv;
   const int g = a.group;
@@ -215,9 +256,45 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   }
 
   // ---- tile addressing -------------------------------------------------------------------------
+  // A tile's rows sit at a uniform base (scalar arithmetic) plus per-lane 32-bit byte offsets
+  // that are the same for every full tile. Only the last, partial tile of a sequence recomputes
+  // them, with the row index clamped to its last valid row, so no lane ever addresses a
+  // position at or past the sequence length.
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
-  int bt_vec = 0, bt_base = -64;  // block ids of this wave's tiles bt_base .. bt_base+63, one per lane
+  const int64_t k_head = int64_t(kvh) * a.k_sh;
+  const int64_t v_head = int64_t(kvh) * a.v_sh;
+  struct LaneOffsets {
+    int k;        // variant 1: key row r16, elements q4*8 (the first 32-element chunk)
+    int kr[4];    // variant 0: key rows 4*q4+i, elements r16*EPL
+    int v[4];     // value rows 4*q4+i, elements r16*EPL
+  };
+  auto lane_offsets = [&](int last) __attribute__((always_inline)) {
+    LaneOffsets o;
+    o.k = (min(r16, last) * int(a.k_st) + q4 * 8) * KVB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(4 * q4 + i, last);
+      o.kr[i] = (row * int(a.k_st) + r16 * EPL) * KVB;
+      o.v[i] = (row * int(a.v_st) + r16 * EPL) * KVB;
+    }
+    return o;
+  };
+  const LaneOffsets full = lane_offsets(kTile - 1);
+
+  // Paged caches: the block ids of this wave's tiles k0 .. k0+63 sit one per lane in bt_vec and
+  // are read with a (scalar) lane read. Consuming the register right after it is loaded makes the
+  // compiler wait for that load there, so the tile loads in the streaming loop never wait on it.
+  int bt_vec = 0, bt_base = 0;
+  auto fetch_block_ids = [&](int k0) __attribute__((always_inline)) {
+    const int kk = k0 + lane;
+    int blk = 0;
+    if (kk < n_w)
+      blk = a.block_table[int64_t(b) * a.max_blocks + (((first + kWaves * kk) * kTile) >> a.bs_log2)];
+    bt_vec = blk;
+    bt_base = k0;
+    asm volatile("" ::"v"(bt_vec));
+  };
 
   struct Frag {
     u32x4_t kc[KC];      // variant 1: key row r16, 32-element chunks
@@ -228,44 +305,30 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   auto load_tile = [&](int k, Frag& f) __attribute__((always_inline)) {
     const int tile = first + kWaves * k;
     const int p0 = tile * kTile;
-    const int last = ctx - 1 - p0;  // >= 0: rows past it are clamped to it
+    const int last = ctx - 1 - p0;  // >= 0; rows past it are clamped to it
     int64_t koff, voff;             // element offset of tile row 0
     if (paged) {
-      if (k - bt_base >= 64) {
-        const int kk = (k & ~63) + lane;
-        int blk = 0;
-        if (kk < n_w)
-          blk = a.block_table[int64_t(b) * a.max_blocks + (((first + kWaves * kk) * kTile) >> a.bs_log2)];
-        bt_vec = blk;
-        bt_base = k & ~63;
-      }
+      if (k - bt_base >= 64) fetch_block_ids(k & ~63);
       const int blk = __builtin_amdgcn_readlane(bt_vec, k - bt_base);
       const int slot0 = p0 & ((1 << a.bs_log2) - 1);
-      koff = int64_t(blk) * a.k_sb + int64_t(slot0) * a.k_st + int64_t(kvh) * a.k_sh;
-      voff = int64_t(blk) * a.v_sb + int64_t(slot0) * a.v_st + int64_t(kvh) * a.v_sh;
+      koff = int64_t(blk) * a.k_sb + int64_t(slot0) * a.k_st + k_head;
+      voff = int64_t(blk) * a.v_sb + int64_t(slot0) * a.v_st + v_head;
     } else {
-      koff = int64_t(b) * a.k_sb + int64_t(p0) * a.k_st + int64_t(kvh) * a.k_sh;
-      voff = int64_t(b) * a.v_sb + int64_t(p0) * a.v_st + int64_t(kvh) * a.v_sh;
+      koff = int64_t(b) * a.k_sb + int64_t(p0) * a.k_st + k_head;
+      voff = int64_t(b) * a.v_sb + int64_t(p0) * a.v_st + v_head;
     }
     const char* kt = kbase + koff * KVB;
     const char* vt = vbase + voff * KVB;
+    const LaneOffsets o = last >= kTile - 1 ? full : lane_offsets(last);
     if constexpr (MFMA) {
-      const int row = min(r16, last);
-      const char* kr = kt + (int64_t(row) * a.k_st + q4 * 8) * 2;
 #pragma unroll
-      for (int c = 0; c < KC; ++c) f.kc[c] = *reinterpret_cast<const u32x4_t*>(kr + c * 64);
+      for (int c = 0; c < KC; ++c) f.kc[c] = load_stream16(kt + o.k + c * 64);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(4 * q4 + i, last);
-        f.kr[i] = load_seg<SEG>(kt + (int64_t(row) * a.k_st + r16 * EPL) * KVB);
-      }
+      for (int i = 0; i < 4; ++i) f.kr[i] = load_seg<SEG>(kt + o.kr[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = min(4 * q4 + i, last);
-      f.vr[i] = load_seg<SEG>(vt + (int64_t(row) * a.v_st + r16 * EPL) * KVB);
-    }
+    for (int i = 0; i < 4; ++i) f.vr[i] = load_seg<SEG>(vt + o.v[i]);
   };
 
   auto compute_tile = [&](int k, const Frag& f) __attribute__((always_inline)) {
@@ -285,8 +348,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[r] = (4 * q4 + r < nvalid) ? acc[r] * a.scale_log2 : neg_inf();
       float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      mt = fmaxf(mt, lane_xor(mt, 16));
-      mt = fmaxf(mt, lane_xor(mt, 32));
+      mt = max_xor32(max_xor16(mt));
       const float m_new = fmaxf(m_run, mt);
       const float c = exp2_fast(m_run - m_new);  // 0 on the first tile (m_run = -inf)
 #pragma unroll
@@ -322,8 +384,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         float mt = fmaxf(fmaxf(s[0][j], s[1][j]), fmaxf(s[2][j], s[3][j]));
-        mt = fmaxf(mt, lane_xor(mt, 16));
-        mt = fmaxf(mt, lane_xor(mt, 32));
+        mt = max_xor32(max_xor16(mt));
         const float m_new = fmaxf(m_v[j], mt);
         cv[j] = exp2_fast(m_v[j] - m_new);
         m_v[j] = m_new;
@@ -357,18 +418,44 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
     }
   };
 
-  // ---- streaming loop: kDepth tiles in flight ------------------------------------------------
+  // ---- streaming loop: kDepth tiles in flight --------------------------------------------------
+  // The steady-state loop issues its loads unconditionally, so the compiler's wait counts let
+  // the kDepth tiles behind the one being computed stay in flight; the last tiles are drained
+  // with conditional loads outside it.
   Frag buf[kDepth];
-  static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
-    if (P() < n_w) load_tile(P(), buf[P()]);
-  });
-  for (int k0 = 0; k0 < n_w; k0 += kDepth) {
+  if (paged && n_w > 0) fetch_block_ids(0);
+  int k0 = 0;
+  if (n_w >= 2 * kDepth) {
+    static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) { load_tile(P(), buf[P()]); });
+    do {
+      static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+        compute_tile(k0 + P(), buf[P()]);
+        load_tile(k0 + P() + kDepth, buf[P()]);
+      });
+      k0 += kDepth;
+    } while (k0 + 2 * kDepth <= n_w);
+    // Tiles k0 .. k0+kDepth-1 are in flight; at most kDepth-1 more remain after them.
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
       const int k = k0 + P();
-      if (k < n_w) {
-        compute_tile(k, buf[P()]);
-        if (k + kDepth < n_w) load_tile(k + kDepth, buf[P()]);
+      compute_tile(k, buf[P()]);
+      if (k + kDepth < n_w) load_tile(k + kDepth, buf[P()]);
+    });
+    static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+      const int k = k0 + kDepth + P();
+      if (k < n_w) compute_tile(k, buf[P()]);
+    });
+  } else {
+    static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+      if (P() < n_w) load_tile(P(), buf[P()]);
+    });
+    static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+      if (P() < n_w) {
+        compute_tile(P(), buf[P()]);
+        if (P() + kDepth < n_w) load_tile(P() + kDepth, buf[P()]);
       }
+    });
+    static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
+      if (kDepth + P() < n_w) compute_tile(kDepth + P(), buf[P()]);
     });
   }
 
@@ -377,8 +464,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   __shared__ float sm_l[kWaves][G];
   __shared__ float sm_o[kWaves][G][D];
   if constexpr (MFMA) {
-    float lt = l_run + lane_xor(l_run, 16);
-    lt += lane_xor(lt, 32);
+    const float lt = sum_xor32(sum_xor16(l_run));
     if (q4 == 0 && r16 < G) {
       sm_m[wave][r16] = m_run;
       sm_l[wave][r16] = lt;
@@ -386,8 +472,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   } else {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float lt = l_v[j] + lane_xor(l_v[j], 16);
-      lt += lane_xor(lt, 32);
+      const float lt = sum_xor32(sum_xor16(l_v[j]));
       if (lane == 0) {
         sm_m[wave][j] = m_v[j];
         sm_l[wave][j] = lt;
@@ -397,10 +482,13 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
 #pragma unroll
   for (int j = 0; j < G; ++j) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float o = O[j][e] + lane_xor(O[j][e], 16);
-      o += lane_xor(o, 32);
-      if (q4 == 0) sm_o[wave][j][r16 * EPL + e] = o;
+    for (int e = 0; e < EPL; ++e) O[j][e] = sum_xor32(sum_xor16(O[j][e]));
+  }
+  if (q4 == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_o[wave][j][r16 * EPL + e] = O[j][e];
     }
   }
   __syncthreads();
@@ -433,13 +521,35 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   }
 }
 
-// Second pass: one wave per (sequence, query head) row merges that row's split states.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) x = fmaxf(x, lane_xor(x, mask));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int mask = 32; mask >= 1; mask >>= 1) x += lane_xor(x, mask);
+  return x;
+}
+
+// Second pass: one workgroup per (sequence, query head) row merges that row's split states,
+// with the rescale-and-add step of the online-softmax recurrence applied to whole states:
+// M = max_s m_s, w_s = 2^(m_s - M) (0 for an empty state), out = sum_s w_s O_s / sum_s w_s l_s.
+// Threads first share the maxima and weights of all splits, then each output element is
+// accumulated over kMergeThreads / D interleaved subsets of splits (independent loads in flight)
+// and the subsets are added in a fixed order.
 template <int D>
-__global__ __launch_bounds__(64 * kMergeRowsPerBlock) void merge_kernel(const MergeArgs a) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a) {
+  constexpr int SUB = kMergeThreads / D;
+  constexpr int NW = kMergeThreads / 64;
+  __shared__ float s_w[kMaxSplits];
+  __shared__ float s_red[NW];
+  __shared__ float s_acc[SUB][D];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int row = blockIdx.x;
   const int S = a.num_splits;
   int nv = S;
   if (a.num_valid != nullptr) {
@@ -453,27 +563,53 @@ __global__ __launch_bounds__(64 * kMergeRowsPerBlock) void merge_kernel(const Me
   const float* ml = a.ml_part + int64_t(row) * S * 2;
   const float* o = a.o_part + int64_t(row) * S * D;
 
-  float M = neg_inf();
-  for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
+  float m_loc = neg_inf();
+  for (int s = tid; s < nv; s += kMergeThreads) m_loc = fmaxf(m_loc, ml[2 * s]);
+  m_loc = wave_max(m_loc);
+  if (lane == 0) s_red[wave] = m_loc;
+  __syncthreads();
+  float M = s_red[0];
 #pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) M = fmaxf(M, lane_xor(M, mask));
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w]);
+  __syncthreads();
 
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  if (M != neg_inf()) {
-    for (int s = 0; s < nv; ++s) {
-      const float m = ml[2 * s];
-      const float w = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
-      L = fmaf(w, ml[2 * s + 1], L);
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[int64_t(s) * D + lane + 64 * e], acc[e]);
-    }
+  float l_loc = 0.f;
+  for (int s = tid; s < nv; s += kMergeThreads) {
+    const float m = ml[2 * s];
+    const float w = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
+    s_w[s] = w;
+    l_loc = fmaf(w, ml[2 * s + 1], l_loc);
   }
+  l_loc = wave_sum(l_loc);
+  if (lane == 0) s_red[wave] = l_loc;
+  __syncthreads();
+  float L = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e)
-    a.out[int64_t(row) * D + lane + 64 * e] = L > 0.f ? acc[e] / L : 0.f;
+  for (int w = 0; w < NW; ++w) L += s_red[w];
+
+  const int e = tid % D;
+  const int sub = tid / D;
+  float acc = 0.f;
+  int s = sub;
+  for (; s + 3 * SUB < nv; s += 4 * SUB) {
+    const float o0 = o[int64_t(s) * D + e];
+    const float o1 = o[int64_t(s + SUB) * D + e];
+    const float o2 = o[int64_t(s + 2 * SUB) * D + e];
+    const float o3 = o[int64_t(s + 3 * SUB) * D + e];
+    acc = fmaf(s_w[s], o0, acc);
+    acc = fmaf(s_w[s + SUB], o1, acc);
+    acc = fmaf(s_w[s + 2 * SUB], o2, acc);
+    acc = fmaf(s_w[s + 3 * SUB], o3, acc);
+  }
+  for (; s < nv; s += SUB) acc = fmaf(s_w[s], o[int64_t(s) * D + e], acc);
+  s_acc[sub][e] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float total = s_acc[0][tid];
+#pragma unroll
+    for (int k = 1; k < SUB; ++k) total += s_acc[k][tid];
+    a.out[int64_t(row) * D + tid] = L > 0.f ? total / L : 0.f;
+  }
 }
 
 template <int D, int G, bool QB, bool KB, bool MF, int PG>
@@ -521,11 +657,12 @@ int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged,
 
 int launch_merge(const MergeArgs& a, int head_dim, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const uint32_t grid = uint32_t((int64_t(a.rows) + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock);
+  if (a.num_splits > kMaxSplits) return int(hipErrorInvalidValue);
+  const uint32_t grid = uint32_t(a.rows);
   if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(64 * kMergeRowsPerBlock), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, s, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(64 * kMergeRowsPerBlock), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, s, a);
   else
     return int(hipErrorInvalidValue);
   return int(hipGetLastError());

@@ -51,6 +51,10 @@ kv_attn_status validate_params(const kv_attn_params* p) {
     // Every row starts 16-byte aligned so that each lane issues whole 128-bit loads.
     if ((s * eb) % 16 != 0) return KV_ATTN_ERR_UNSUPPORTED;
   }
+  // Rows inside one 16-position tile are addressed with 32-bit byte offsets.
+  if (p->k_stride_token * eb * kTile >= (int64_t(1) << 31) ||
+      p->v_stride_token * eb * kTile >= (int64_t(1) << 31))
+    return KV_ATTN_ERR_UNSUPPORTED;
   return KV_ATTN_OK;
 }
 
@@ -104,7 +108,7 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   plan->variant = (p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector) ? 1 : 0;
   plan->grid_split = units * S;
   const int64_t rows = int64_t(p->batch) * p->num_q_heads;
-  plan->grid_merge = S > 1 ? ceil_div(rows, kMergeRowsPerBlock) : 0;
+  plan->grid_merge = S > 1 ? rows : 0;
   if (S > 1) {
     const uint64_t o_bytes = uint64_t(rows) * uint64_t(S) * uint64_t(p->head_dim) * 4u;
     const uint64_t o_aligned = (o_bytes + 255u) & ~uint64_t(255u);

@@ -37,7 +37,9 @@ __all__ = [
     "EXPORTED_SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvattn.so")
+# KV_ATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("KV_ATTN_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libkvattn.so")
 
 KV_ATTN_OK = 0
 KV_ATTN_ERR_NULL = 1

@@ -111,7 +111,7 @@ def test_plan_covers_every_tile_and_respects_bounds():
             if S > 1:
                 assert L // 16 >= min(16, tiles)             # splits of >= 16 tiles when possible
                 assert plan["workspace_bytes"] >= B * hkv * 2 * S * (128 + 2) * 4
-                assert plan["grid_merge"] == (B * hkv * 2 + 3) // 4
+                assert plan["grid_merge"] == B * hkv * 2
             else:
                 assert plan["workspace_bytes"] == 0 and plan["grid_merge"] == 0
             assert L // 16 <= 256 or S == 4096
@@ -121,10 +121,10 @@ def test_plan_for_the_five_workloads():
     """Launch geometry of C1-C5 on a 256-CU device (what the bench times)."""
     want = {  # (B, h_q, h_kv, T) -> (S, split_len)
         (1, 8, 8, 256): (1, 256),
-        (8, 32, 32, 4096): (8, 512),
-        (64, 32, 8, 8192): (4, 2048),
+        (8, 32, 32, 4096): (4, 1024),
+        (64, 32, 8, 8192): (2, 4096),
         (128, 32, 8, 32768): (8, 4096),
-        (4, 64, 8, 131072): (64, 2048),
+        (4, 64, 8, 131072): (32, 4096),
     }
     for (B, hq, hkv, T), (S, L) in want.items():
         p = _params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
@@ -181,6 +181,7 @@ def test_merge_argument_errors():
     assert lib.kv_attn_merge(16, 16, None, 16, 0, 2, 128, None) == K.KV_ATTN_ERR_SHAPE
     assert lib.kv_attn_merge(16, 16, None, 16, 4, 0, 128, None) == K.KV_ATTN_ERR_SHAPE
     assert lib.kv_attn_merge(16, 16, None, 16, 4, 2, 100, None) == K.KV_ATTN_ERR_UNSUPPORTED
+    assert lib.kv_attn_merge(16, 16, None, 16, 4, 4097, 128, None) == K.KV_ATTN_ERR_UNSUPPORTED
 
 
 def test_host_validator():
