@@ -12,10 +12,11 @@ Measurement (Ch. 10 "System Model of Throughput and Latency" §8: warm up, time 
 with events, never time host submission):
   * pass A: W warm-up steps, then K steps bracketed by device events on the launch stream, with
     torch.cuda.synchronize() on both sides -> ms_per_step, value = unique KV bytes / step time;
-  * pass B: K more steps with events around every split-kernel launch -> that kernel's average
-    duration, and roofline.achieved = its unique KV bytes per launch / that duration;
+  * pass B: K more steps whose split-kernel launches run back to back between device events ->
+    that kernel's average duration, and roofline.achieved = its unique KV bytes per launch /
+    that duration (the merge launches follow outside the events);
   * cpu_baseline: the fp64 oracle (oracle/) timed on the host on a bounded sample of the same
-    workload (whole (sequence, KV head) units of layer 0, about 15 s of CPU work).
+    workload (whole (layer, sequence, KV head) units in order, about 15 s of CPU work).
 
 Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -35,13 +36,18 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (unique KV bytes/time) + decode-attn µs/step"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "kv_cache_decode_split_amd", "csrc", "kv_attn_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_decode_split_amd", "csrc", f)
+                  for f in ("kv_attn_kernels.hip", "kv_attn_internal.h", "kv_attn_plan.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the sources that decide what the split kernel reads and writes."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(workload: str):
@@ -93,12 +99,10 @@ def main():
     print(f"[bench] building {args.config} ({layers} layer(s)) on the GPU", file=sys.stderr, flush=True)
     wls = [W.make_workload(spec, device="cuda", layer=l) for l in range(layers)]
     outs = [torch.empty(w.q.shape, dtype=torch.float32, device="cuda") for w in wls]
-    probe = K.decode_call_for(wls[0], outs[0], num_splits=args.num_splits)
-    plan = probe.plan()
-    ws = (torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
-          if plan["workspace_bytes"] else None)
-    calls = [K.decode_call_for(w, o, num_splits=args.num_splits, workspace=ws)
-             for w, o in zip(wls, outs)]
+    # One call (and workspace) per layer, so that pass B can run all split launches before the
+    # merges without one layer's split states overwriting another's.
+    calls = [K.decode_call_for(w, o, num_splits=args.num_splits) for w, o in zip(wls, outs)]
+    plan = calls[0].plan()
     elem = 2 if spec.kv_dtype == "bf16" else 4
     lens = [int(x) for x in wls[0].ctx_lens.cpu().tolist()]
     kv_bytes_layer = A.unique_kv_read_bytes(lens, spec.num_kv_heads, spec.head_dim, elem)
@@ -130,20 +134,23 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] pass A done: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    # ---- pass B: per-launch events around the split kernel ---------------------------------------
-    evs = []
+    # ---- pass B: the split kernel alone, launched back to back ------------------------------------
+    # Events bracket each step's run of split launches (one per layer, same stream, nothing in
+    # between), so the average launch duration carries no per-launch event overhead.
+    split_ms = []
     torch.cuda.synchronize()
     for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
         for c in calls:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
             c.split()
-            b.record()
+        b.record()
+        for c in calls:  # keep the outputs complete (merge pass), outside the bracket
             c.merge()
-            evs.append((a, b))
+        split_ms.append((a, b))
     torch.cuda.synchronize()
-    split_ms = [a.elapsed_time(b) for a, b in evs]
+    split_ms = [a.elapsed_time(b) / len(calls) for a, b in split_ms]
     split_us_avg = 1e3 * sum(split_ms) / len(split_ms)
     print(f"[bench] pass B done: split kernel {split_us_avg:.1f} us/launch", file=sys.stderr, flush=True)
 
@@ -157,7 +164,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wls[0], spec, args.cpu_seconds, elem)
+        cpu = cpu_baseline(wls, spec, args.cpu_seconds, elem)
 
     achieved = kv_bytes_layer / (split_us_avg * 1e-6) / 1e9
     traffic, traffic_src = load_traffic(args.config)
@@ -198,7 +205,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_us": round(split_us_avg, 2),
-            "launches_timed": len(split_ms),
+            "launches_timed": len(split_ms) * len(calls),
         },
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "outputs_finite": finite,
@@ -218,22 +225,24 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(w, spec, budget_s, elem):
-    """The oracle, as it stands, on whole (sequence, KV head) units of layer 0 until the time
-    budget is spent (at least one unit). Returns unique-KV GB/s of the oracle."""
+def cpu_baseline(wls, spec, budget_s, elem):
+    """The oracle, as it stands, on whole (layer, sequence, KV head) units of the workload, in
+    order, until the time budget is spent (at least one unit). Host copies of each unit are made
+    outside the timed region. Returns the oracle's unique-KV GB/s."""
     from kv_cache_decode_split_amd import workloads as W
     from oracle import decode_attention
 
-    units = [(b, h) for b in range(spec.batch) for h in range(spec.num_kv_heads)]
-    lens = w.ctx_lens.cpu().tolist()
+    units = [(l, b, h) for l in range(len(wls)) for b in range(spec.batch)
+             for h in range(spec.num_kv_heads)]
+    lens = [w.ctx_lens.cpu().tolist() for w in wls]
     done_bytes, spent, n = 0, 0.0, 0
-    for b, h in units:
-        v = W.oracle_sample(w, [b], [h])  # host copy, outside the timed region
+    for l, b, h in units:
+        v = W.oracle_sample(wls[l], [b], [h])
         t0 = time.perf_counter()
         decode_attention(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
                          block_size=v["block_size"] if v["block_table"] is not None else None)
         spent += time.perf_counter() - t0
-        done_bytes += 2 * int(lens[b]) * spec.head_dim * elem
+        done_bytes += 2 * int(lens[l][b]) * spec.head_dim * elem
         n += 1
         if spent >= budget_s:
             break
@@ -242,8 +251,8 @@ def cpu_baseline(w, spec, budget_s, elem):
         "unit": "GB/s",
         "cores": _blas_threads(),
         "kind": "oracle",
-        "sample": f"{n} of {len(units)} (sequence, KV head) units of layer 0 of {spec.name} "
-                  f"({done_bytes} unique KV bytes, {spent:.1f} s)",
+        "sample": f"{n} of {len(units)} (layer, sequence, KV head) units of {spec.name}, in order "
+                  f"({done_bytes} unique KV bytes, {spent:.1f} s of oracle time)",
     }
 
 
