@@ -10,7 +10,8 @@ last-level cache so every step streams from HBM).
 
 Measurement (Ch. 10 "System Model of Throughput and Latency" §8: warm up, time on the device
 with events, never time host submission):
-  * pass A: W warm-up steps, then K steps bracketed by device events on the launch stream, with
+  * pass A: W warm-up steps (default: >= 0.25 s of GPU work), then K steps bracketed by device
+    events on the launch stream, with
     torch.cuda.synchronize() on both sides -> ms_per_step, value = unique KV bytes / step time;
   * pass B: K more steps whose split-kernel launches run back to back between device events ->
     that kernel's average duration, and roofline.achieved = its unique KV bytes per launch /
@@ -66,7 +67,8 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="warm-up steps (default: enough for >= 0.25 s of GPU work, at least 5)")
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -120,6 +122,15 @@ def main():
             c.decode()
 
     # ---- pass A: whole steps -------------------------------------------------------------------
+    # The first tens of milliseconds of sustained load on a fresh device run measurably slower
+    # (kernel durations drift for ~50-100 launches, then settle), so the default warm-up covers
+    # at least 0.25 s of GPU work.
+    if args.warmup is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        args.warmup = max(5, int(0.25 / max(time.perf_counter() - t0, 1e-6)) + 1)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

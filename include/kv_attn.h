@@ -124,7 +124,7 @@ const char* kv_attn_status_string(int32_t status);
  * Plan the launch for `p` as if on a device with `num_cus` compute units (0 = query the
  * current HIP device). Validates `p` exactly as kv_attn_decode does (pointers aside). Split
  * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
- * workgroups number about 4 per compute unit, each split spans 16..256 tiles, and a
+ * workgroups number at least about one per compute unit, each split spans 16..256 tiles, and a
  * caller-given num_splits overrides the count. Writes *plan only on KV_ATTN_OK.
  */
 kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_attn_plan* plan);

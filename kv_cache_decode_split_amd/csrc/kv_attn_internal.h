@@ -21,7 +21,7 @@ constexpr int kMergeThreads = 256;
 // Split planning constants (see make_plan).
 constexpr int kMinSplitTiles = 16;     // a split spans at least 256 positions ...
 constexpr int kMaxSplitTiles = 256;    // ... and at most 4096 positions
-constexpr int kWorkgroupsPerCu = 4;    // target split workgroups per compute unit
+constexpr int kWorkgroupsPerCu = 1;    // target split workgroups per compute unit
 constexpr int kMaxSplits = 4096;
 
 // Everything the split kernel needs, by value.

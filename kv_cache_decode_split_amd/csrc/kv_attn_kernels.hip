@@ -168,9 +168,17 @@ __device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
   }
 }
 
+#ifndef KV_ATTN_WAVES_PER_EU
+#define KV_ATTN_WAVES_PER_EU 0
+#endif
+
 // PAGED: 0 contiguous, 1 paged, 2 decided at run time (vector variant only).
 template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED>
-__global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a) {
+__global__ __launch_bounds__(kSplitThreads)
+#if KV_ATTN_WAVES_PER_EU > 0
+__attribute__((amdgpu_waves_per_eu(MFMA && G <= 8 ? KV_ATTN_WAVES_PER_EU : 1)))
+#endif
+void split_kernel(const SplitArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(!MFMA || (Q_BF16 && KV_BF16), "matrix-core scores need bf16 q and KV");
   constexpr int EPL = D / 16;                 // elements per lane of a 16-lane row

@@ -121,7 +121,7 @@ def test_plan_for_the_five_workloads():
     """Launch geometry of C1-C5 on a 256-CU device (what the bench times)."""
     want = {  # (B, h_q, h_kv, T) -> (S, split_len)
         (1, 8, 8, 256): (1, 256),
-        (8, 32, 32, 4096): (4, 1024),
+        (8, 32, 32, 4096): (1, 4096),
         (64, 32, 8, 8192): (2, 4096),
         (128, 32, 8, 32768): (8, 4096),
         (4, 64, 8, 131072): (32, 4096),
