@@ -148,20 +148,24 @@ def main():
     # ---- pass B: the split kernel alone, launched back to back ------------------------------------
     # Events bracket each step's run of split launches (one per layer, same stream, nothing in
     # between), so the average launch duration carries no per-launch event overhead.
+    # With fewer than 8 layers, each bracket repeats the layer loop so that it holds at least
+    # 8 launches (a lone launch between two events also times the events themselves).
+    reps = max(1, -(-8 // len(calls)))
     split_ms = []
     torch.cuda.synchronize()
     for _ in range(args.steps):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for c in calls:
-            c.split()
+        for _ in range(reps):
+            for c in calls:
+                c.split()
         b.record()
         for c in calls:  # keep the outputs complete (merge pass), outside the bracket
             c.merge()
         split_ms.append((a, b))
     torch.cuda.synchronize()
-    split_ms = [a.elapsed_time(b) / len(calls) for a, b in split_ms]
+    split_ms = [a.elapsed_time(b) / (reps * len(calls)) for a, b in split_ms]
     split_us_avg = 1e3 * sum(split_ms) / len(split_ms)
     print(f"[bench] pass B done: split kernel {split_us_avg:.1f} us/launch", file=sys.stderr, flush=True)
 
@@ -216,7 +220,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_us": round(split_us_avg, 2),
-            "launches_timed": len(split_ms) * len(calls),
+            "launches_timed": len(split_ms) * len(calls) * reps,
         },
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "outputs_finite": finite,
