@@ -73,6 +73,8 @@ def parse_args():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
+    ap.add_argument("--append", action="store_true",
+                    help="each layer first appends the current token's K/V (kv_attn_append_decode)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run plain device copies of this size (counter calibration runs)")
     return ap.parse_args()
@@ -117,9 +119,21 @@ def main():
         calib = (torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1),
                  torch.empty(n, dtype=torch.uint8, device="cuda"))
 
+    news = []
+    if args.append:  # the current token's K/V row for every layer (written at ctx_lens[b] - 1)
+        g = torch.Generator(device="cuda").manual_seed(4242)
+        for w in wls:
+            shape = (spec.batch, spec.num_kv_heads, spec.head_dim)
+            news.append(tuple(torch.randn(shape, generator=g, device="cuda").to(w.k_cache.dtype)
+                              for _ in range(2)))
+
     def step():
-        for c in calls:
-            c.decode()
+        if args.append:
+            for c, (kn, vn) in zip(calls, news):
+                c.append_decode(kn, vn)
+        else:
+            for c in calls:
+                c.decode()
 
     # ---- pass A: whole steps -------------------------------------------------------------------
     # The first tens of milliseconds of sustained load on a fresh device run measurably slower
@@ -168,6 +182,31 @@ def main():
     split_ms = [a.elapsed_time(b) / (reps * len(calls)) for a, b in split_ms]
     split_us_avg = 1e3 * sum(split_ms) / len(split_ms)
     print(f"[bench] pass B done: split kernel {split_us_avg:.1f} us/launch", file=sys.stderr, flush=True)
+
+    append_info = None
+    if args.append:  # the append kernel alone, launched back to back
+        positions = [(w.ctx_lens - 1).to(torch.int32) for w in wls]
+        ks_vs = [w.kv_strides() for w in wls]
+
+        def append_all():
+            for w, (kn, vn), pos, (ks, vs) in zip(wls, news, positions, ks_vs):
+                K.kv_attn_append(kn, vn, w.k_cache, w.v_cache, w.block_table, pos,
+                                 num_kv_heads=spec.num_kv_heads, k_strides=ks, v_strides=vs,
+                                 block_size=w.block_size, num_blocks=w.num_blocks)
+        append_all()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps * args.steps):
+            append_all()
+        b.record()
+        torch.cuda.synchronize()
+        n = reps * args.steps * len(wls)
+        row_bytes = spec.batch * spec.num_kv_heads * spec.head_dim * elem
+        append_info = {"avg_launch_us": round(a.elapsed_time(b) * 1e3 / n, 3),
+                       "bytes_written_per_launch": 2 * row_bytes,
+                       "bytes_read_per_launch": 2 * row_bytes, "launches_timed": n}
 
     if calib is not None:  # plain copies of known size, for the counter-calibration runs
         for _ in range(4):
@@ -226,6 +265,9 @@ def main():
         "outputs_finite": finite,
         "cpu_baseline": cpu,
     }
+    if args.append:
+        line["config"]["append"] = "each layer appends the current token's K/V before attending"
+        line["append"] = append_info
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
     print(json.dumps(line), flush=True)

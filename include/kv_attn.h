@@ -196,6 +196,37 @@ kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
                              int32_t num_splits, int32_t head_dim, void* stream);
 
 /*
+ * Append one token's K and V rows per sequence to the cache: the step that precedes attention
+ * in every decode step (Ch. 10 §4 counts this new-KV write; Ch. 19 §19.7.3 grows a paged cache
+ * block by block through the block table).
+ *
+ * k_new, v_new : device, kv_dtype, contiguous [batch, num_kv_heads, head_dim], 16-byte aligned.
+ * k_cache,
+ * v_cache      : the caches described by p (strides, block_size, block_table as for decode);
+ *                written in place at one slot per (sequence, KV head) and nowhere else.
+ * positions    : device int32 [batch]: logical position written for sequence b, through
+ *                block_table[b][pos / block_size] (paged) or slot pos of sequence b
+ *                (contiguous). A negative position (idle sequence) or one at or past the
+ *                capacity (max_blocks_per_seq * block_size, or block_size when contiguous) writes
+ *                nothing. The block that holds the position must already be in the table.
+ * Enqueued on `stream`; the rows of a sequence must not be read by other work in flight.
+ */
+kv_attn_status kv_attn_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_table, const int32_t* positions,
+                              const kv_attn_params* p, void* stream);
+
+/*
+ * kv_attn_append then kv_attn_decode in one call: the new token of sequence b is the last
+ * position ctx_lens[b] counts, so it is written at position ctx_lens[b] - 1 (nothing for an empty
+ * sequence) and then attended together with the cached ones. Arguments as for the two calls;
+ * every check of both runs before anything is launched.
+ */
+kv_attn_status kv_attn_append_decode(const void* q, const void* k_new, const void* v_new,
+                                     void* k_cache, void* v_cache, const int32_t* block_table,
+                                     const int32_t* ctx_lens, float* out, const kv_attn_params* p,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Host-side check of the device-resident inputs' contents (debug aid; runs on the CPU and
  * touches no device): every 0 <= ctx_lens[b] <= max_ctx_len and, for a paged cache
  * (block_table != NULL), every entry 0 <= block_table[b][i] < num_blocks for

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <vector>
 
@@ -105,16 +106,49 @@ namespace {
 
 constexpr int kPassSplit = 1;
 constexpr int kPassMerge = 2;
+constexpr int kPassAppend = 4;
+
+AppendArgs append_args(const kv_attn_params* p, const void* k_new, const void* v_new, void* k,
+                       void* v, const int32_t* block_table, const int32_t* positions,
+                       int32_t pos_offset) {
+  const bool paged = block_table != nullptr;
+  const int eb = p->kv_dtype == KV_ATTN_BF16 ? 2 : 4;
+  AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k = k;
+  a.v = v;
+  a.block_table = block_table;
+  a.positions = positions;
+  a.k_sb = p->k_stride_block;
+  a.k_st = p->k_stride_token;
+  a.k_sh = p->k_stride_head;
+  a.v_sb = p->v_stride_block;
+  a.v_st = p->v_stride_token;
+  a.v_sh = p->v_stride_head;
+  a.h_kv = p->num_kv_heads;
+  a.row_chunks = p->head_dim * eb / 16;
+  a.elem_bytes = eb;
+  a.bs_log2 = paged ? log2_exact(p->block_size) : 0;
+  a.max_blocks = paged ? p->max_blocks_per_seq : 0;
+  a.limit = paged ? int32_t(std::min<int64_t>(int64_t(p->max_blocks_per_seq) * p->block_size, 0x7fffffff))
+                  : p->block_size;
+  a.pos_offset = pos_offset;
+  a.total = p->batch * p->num_kv_heads * a.row_chunks;
+  return a;
+}
 
 // Shared body of kv_attn_decode / _split / _merge: validation, planning, then the passes in
 // `passes`. Every host-side check runs before the first HIP call.
 kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* ctx_lens, float* out,
                            const kv_attn_params* p, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           void* stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   if (p == nullptr || ctx_lens == nullptr || out == nullptr) return KV_ATTN_ERR_NULL;
   if ((passes & kPassSplit) && (q == nullptr || k_cache == nullptr || v_cache == nullptr))
     return KV_ATTN_ERR_NULL;
+  if ((passes & kPassAppend) && (k_new == nullptr || v_new == nullptr)) return KV_ATTN_ERR_NULL;
+  if ((passes & kPassAppend) && (!aligned16(k_new) || !aligned16(v_new))) return KV_ATTN_ERR_UNSUPPORTED;
   const bool paged = block_table != nullptr;
   kv_attn_status st = (passes & kPassSplit) ? validate_layout(p, paged) : validate_params(p);
   if (st != KV_ATTN_OK) return st;
@@ -144,6 +178,12 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
                        ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.o_part_bytes)
                        : nullptr;
 
+  if (passes & kPassAppend) {
+    // The current token is the last position ctx_lens[b] counts: write it before reading.
+    const AppendArgs ap = append_args(p, k_new, v_new, const_cast<void*>(k_cache),
+                                      const_cast<void*>(v_cache), block_table, ctx_lens, -1);
+    if (launch_append(ap, stream) != 0) return KV_ATTN_ERR_HIP;
+  }
   if (passes & kPassSplit) {
     SplitArgs a;
     a.q = q;
@@ -219,6 +259,38 @@ kv_attn_status kv_attn_decode_merge(const int32_t* ctx_lens, float* out, const k
                                     void* workspace, size_t workspace_bytes, void* stream) {
   return kvattn::decode_impl(kvattn::kPassMerge, nullptr, nullptr, nullptr, nullptr, ctx_lens, out,
                              p, workspace, workspace_bytes, stream);
+}
+
+kv_attn_status kv_attn_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_table, const int32_t* positions,
+                              const kv_attn_params* p, void* stream) {
+  if (p == nullptr || k_new == nullptr || v_new == nullptr || k_cache == nullptr ||
+      v_cache == nullptr || positions == nullptr)
+    return KV_ATTN_ERR_NULL;
+  const kv_attn_status st = kvattn::validate_layout(p, block_table != nullptr);
+  if (st != KV_ATTN_OK) return st;
+  if (!kvattn::aligned16(k_new) || !kvattn::aligned16(v_new) || !kvattn::aligned16(k_cache) ||
+      !kvattn::aligned16(v_cache))
+    return KV_ATTN_ERR_UNSUPPORTED;
+  if (kvattn::fault_injected("launch")) return KV_ATTN_ERR_HIP;
+  const kvattn::AppendArgs a =
+      kvattn::append_args(p, k_new, v_new, k_cache, v_cache, block_table, positions, 0);
+  if (kvattn::launch_append(a, stream) != 0) return KV_ATTN_ERR_HIP;
+  if (kvattn::debug_mode()) {
+    if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess ||
+        hipGetLastError() != hipSuccess)
+      return KV_ATTN_ERR_HIP;
+  }
+  return KV_ATTN_OK;
+}
+
+kv_attn_status kv_attn_append_decode(const void* q, const void* k_new, const void* v_new,
+                                     void* k_cache, void* v_cache, const int32_t* block_table,
+                                     const int32_t* ctx_lens, float* out, const kv_attn_params* p,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return kvattn::decode_impl(kvattn::kPassAppend | kvattn::kPassSplit | kvattn::kPassMerge, q,
+                             k_cache, v_cache, block_table, ctx_lens, out, p, workspace,
+                             workspace_bytes, stream, k_new, v_new);
 }
 
 kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,

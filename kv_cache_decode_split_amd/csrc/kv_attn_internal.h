@@ -60,6 +60,27 @@ struct MergeArgs {
   int32_t max_ctx;             // decode path: clamp of ctx_lens
 };
 
+// Everything the append kernel needs: one new K/V row per (sequence, KV head) is stored at
+// logical position positions[b] + pos_offset of sequence b.
+struct AppendArgs {
+  const void* k_new;           // [B, h_kv, d] contiguous
+  const void* v_new;
+  void* k;                     // caches (same layout rules as the split kernel)
+  void* v;
+  const int32_t* block_table;  // nullptr: contiguous cache
+  const int32_t* positions;    // [B]
+  int64_t k_sb, k_st, k_sh;
+  int64_t v_sb, v_st, v_sh;
+  int32_t h_kv;
+  int32_t row_chunks;          // 16-byte pieces per row: d * elem_bytes / 16
+  int32_t elem_bytes;
+  int32_t bs_log2;             // paged only
+  int32_t max_blocks;          // paged only
+  int32_t limit;               // positions at or past it are not written
+  int32_t pos_offset;          // 0, or -1 when positions are context lengths
+  int32_t total;               // B * h_kv * row_chunks
+};
+
 struct Plan {
   int32_t num_splits;
   int32_t split_tiles;
@@ -83,6 +104,7 @@ bool fault_injected(const char* where);  // KV_ATTN_FAULT=<where>: simulate a HI
 int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, bool q_bf16,
                  bool kv_bf16, void* stream);
 int launch_merge(const MergeArgs& a, int head_dim, void* stream);
+int launch_append(const AppendArgs& a, void* stream);
 
 }  // namespace kvattn
 

@@ -620,6 +620,35 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
   }
 }
 
+// Append: one thread per 16-byte piece of a new K (and V) row. The destination follows the
+// block-table translation of the new token's logical position, exactly as the split kernel reads
+// it back; negative positions (idle sequences) and positions at or past the capacity are skipped.
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  const int idx = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (idx >= a.total) return;
+  const int chunk = idx % a.row_chunks;
+  const int row = idx / a.row_chunks;  // b * h_kv + kvh
+  const int kvh = row % a.h_kv;
+  const int b = row / a.h_kv;
+  const int pos = a.positions[b] + a.pos_offset;
+  if (pos < 0 || pos >= a.limit) return;
+  int64_t blk, slot;
+  if (a.block_table != nullptr) {
+    blk = a.block_table[int64_t(b) * a.max_blocks + (pos >> a.bs_log2)];
+    slot = pos & ((1 << a.bs_log2) - 1);
+  } else {
+    blk = b;
+    slot = pos;
+  }
+  const int64_t src = (int64_t(row) * a.row_chunks + chunk) * 16;
+  const int64_t kdst = (blk * a.k_sb + slot * a.k_st + int64_t(kvh) * a.k_sh) * a.elem_bytes + chunk * 16;
+  const int64_t vdst = (blk * a.v_sb + slot * a.v_st + int64_t(kvh) * a.v_sh) * a.elem_bytes + chunk * 16;
+  const u32x4_t kx = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(a.k_new) + src);
+  const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(a.v_new) + src);
+  *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(a.k) + kdst) = kx;
+  *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(a.v) + vdst) = vx;
+}
+
 template <int D, int G, bool QB, bool KB, bool MF, int PG>
 int launch_one(const SplitArgs& a, int64_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG>), dim3(uint32_t(grid)), dim3(kSplitThreads),
@@ -661,6 +690,14 @@ int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged,
   if (head_dim == 64) return launch_group<64>(a, plan, paged, q_bf16, kv_bf16, s);
   if (head_dim == 128) return launch_group<128>(a, plan, paged, q_bf16, kv_bf16, s);
   return int(hipErrorInvalidValue);
+}
+
+int launch_append(const AppendArgs& a, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (a.total <= 0) return 0;
+  const uint32_t grid = uint32_t((int64_t(a.total) + 255) / 256);
+  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(256), 0, s, a);
+  return int(hipGetLastError());
 }
 
 int launch_merge(const MergeArgs& a, int head_dim, void* stream) {

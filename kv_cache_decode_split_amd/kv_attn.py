@@ -30,6 +30,8 @@ __all__ = [
     "kv_attn_decode_split",
     "kv_attn_decode_merge",
     "kv_attn_decode_workload",
+    "kv_attn_append",
+    "kv_attn_append_decode",
     "DecodeCall",
     "decode_call_for",
     "kv_attn_merge",
@@ -61,6 +63,8 @@ EXPORTED_SYMBOLS = (
     "kv_attn_decode",
     "kv_attn_decode_split",
     "kv_attn_decode_merge",
+    "kv_attn_append",
+    "kv_attn_append_decode",
     "kv_attn_merge",
     "kv_attn_validate_host",
 )
@@ -131,6 +135,11 @@ def _load():
     lib.kv_attn_decode_split.restype = ctypes.c_int
     lib.kv_attn_decode_merge.argtypes = [vp, vp, P(kv_attn_params), vp, ctypes.c_size_t, vp]
     lib.kv_attn_decode_merge.restype = ctypes.c_int
+    lib.kv_attn_append.argtypes = [vp, vp, vp, vp, vp, vp, P(kv_attn_params), vp]
+    lib.kv_attn_append.restype = ctypes.c_int
+    lib.kv_attn_append_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, P(kv_attn_params), vp,
+                                          ctypes.c_size_t, vp]
+    lib.kv_attn_append_decode.restype = ctypes.c_int
     lib.kv_attn_merge.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
     lib.kv_attn_merge.restype = ctypes.c_int
     lib.kv_attn_validate_host.argtypes = [vp, vp, P(kv_attn_params)]
@@ -287,6 +296,24 @@ class DecodeCall:
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode_merge")
 
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        """Write each sequence's new K/V row at position ctx_lens[b] - 1, then decode."""
+        q, k_cache = self._keep[0], self._keep[1]
+        _check_new_rows(k_new, v_new, k_cache, q.shape[0], self.params.num_kv_heads, q.shape[2])
+        st = _lib.kv_attn_append_decode(self._ptrs[0], k_new.data_ptr(), v_new.data_ptr(),
+                                        *self._ptrs[1:], ctypes.byref(self.params), *self._ws,
+                                        _stream_handle(stream))
+        if st != KV_ATTN_OK:
+            raise KvAttnError(st, "kv_attn_append_decode")
+
+
+def _check_new_rows(k_new, v_new, cache, batch, num_kv_heads, head_dim):
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if (t.shape != (batch, num_kv_heads, head_dim) or not t.is_contiguous()
+                or t.dtype != cache.dtype or t.device != cache.device):
+            raise ValueError(f"{name} must be a contiguous [B, h_kv, d] tensor of the cache's "
+                             "dtype on its device")
+
 
 def kv_attn_decode(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None, **kwargs) -> None:
     """Enqueue one decode-attention step (both passes); arguments as for :class:`DecodeCall`."""
@@ -304,6 +331,42 @@ def kv_attn_decode_split(q, k_cache, v_cache, block_table, ctx_lens, out, *, str
 def kv_attn_decode_merge(call: DecodeCall, stream=None) -> None:
     """Enqueue the merge pass over the workspace of a :func:`kv_attn_decode_split` call."""
     call.merge(stream)
+
+
+def kv_attn_append(k_new, v_new, k_cache, v_cache, block_table, positions, *, num_kv_heads: int,
+                   k_strides: Sequence[int], v_strides: Sequence[int], block_size: int,
+                   num_blocks: int, stream=None) -> None:
+    """Store k_new/v_new ([B, h_kv, d]) at logical position positions[b] of every sequence."""
+    B = int(positions.shape[0])
+    d = int(k_new.shape[-1])
+    _check_new_rows(k_new, v_new, k_cache, B, num_kv_heads, d)
+    if positions.dtype != torch.int32 or not positions.is_contiguous() or positions.device != k_cache.device:
+        raise ValueError("positions must be a contiguous int32 [B] tensor on the cache's device")
+    if block_table is not None:
+        if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B
+                or not block_table.is_contiguous() or block_table.device != k_cache.device):
+            raise ValueError("block_table must be a contiguous int32 [B, max_blocks] device tensor")
+        max_blocks = int(block_table.shape[1])
+    else:
+        max_blocks = 1
+    p = make_params(batch=B, num_q_heads=num_kv_heads, num_kv_heads=num_kv_heads, head_dim=d,
+                    block_size=block_size, max_ctx_len=0, num_blocks=num_blocks, k_strides=k_strides,
+                    v_strides=v_strides, max_blocks_per_seq=max_blocks,
+                    kv_dtype=_dtype_code(k_cache.dtype), q_dtype=_dtype_code(k_cache.dtype))
+    _check_extent(k_cache, k_strides, num_blocks, block_size, num_kv_heads, d, "k_cache")
+    _check_extent(v_cache, v_strides, num_blocks, block_size, num_kv_heads, d, "v_cache")
+    st = _lib.kv_attn_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                             v_cache.data_ptr(), None if block_table is None else block_table.data_ptr(),
+                             positions.data_ptr(), ctypes.byref(p), _stream_handle(stream))
+    if st != KV_ATTN_OK:
+        raise KvAttnError(st, "kv_attn_append")
+
+
+def kv_attn_append_decode(q, k_new, v_new, k_cache, v_cache, block_table, ctx_lens, out, *,
+                          stream=None, **kwargs) -> None:
+    """Append each sequence's new K/V at ctx_lens[b] - 1, then decode (one call, same stream)."""
+    DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, **kwargs).append_decode(
+        k_new, v_new, stream)
 
 
 def _workload_args(w) -> dict:

@@ -16,6 +16,9 @@ online_softmax
     reference for the GPU merge step.
 fsum_reference
     A second, pure-Python (math.fsum) implementation of the plain definition for tiny shapes.
+kv_append
+    Writing one new token's K/V rows into a contiguous or block-table cache (the step before
+    attention).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed forms, invariants,
 brute force and the independent pure-Python implementation (no function is "parity unpinned").
@@ -38,3 +41,4 @@ from .online_softmax import (  # noqa: F401
     finalize_state,
 )
 from .fsum_reference import decode_attention_fsum  # noqa: F401
+from .kv_append import append_kv  # noqa: F401

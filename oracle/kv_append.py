@@ -1,0 +1,52 @@
+"""Plain reference for appending one token's K/V rows to a (paged) KV cache.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__.py``).
+
+Sources: Ch. 10 "System Model of Throughput and Latency" (第十章 吞吐与延迟的系统模型) §4 —
+every decode step writes the new token's key and value for every layer and KV head (the new-KV
+write term of the traffic model) and the step reuses them right away; Ch. 19 "Inference
+Systems and Performance Engineering" (第19章 推理系统与性能工程) §19.7.3 — the cache grows block by
+block through the block table, so logical position t of sequence b lives in physical block
+``block_table[b][t // block_size]`` at slot ``t % block_size``.
+
+Reading: a negative position means "this sequence appends nothing this step" (an idle slot in a
+batch); positions at or past the cache's capacity are not written either.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["append_kv"]
+
+
+def append_kv(cache: np.ndarray, new_rows: np.ndarray, positions, block_table=None, *,
+              block_size: int | None = None, capacity: int | None = None) -> np.ndarray:
+    """Return a copy of ``cache`` with ``new_rows[b, kv_head, :]`` stored at logical position
+    ``positions[b]`` of sequence ``b`` for every KV head.
+
+    ``cache`` is indexed ``[block, slot, kv_head, dim]`` (any storage dtype, copied bit for bit);
+    ``new_rows`` is ``[B, h_kv, dim]`` of the same dtype. Without a block table the cache is
+    contiguous per sequence (block ``b``, slot = position) and ``capacity`` bounds the position;
+    with one, ``block_table.shape[1] * block_size`` does.
+    """
+    out = np.array(cache, copy=True)
+    new_rows = np.asarray(new_rows)
+    if new_rows.dtype != out.dtype:
+        raise TypeError("new rows and cache must share a storage dtype")
+    for b, pos in enumerate(np.asarray(positions).tolist()):
+        pos = int(pos)
+        if pos < 0:
+            continue
+        if block_table is None:
+            limit = capacity if capacity is not None else out.shape[1]
+            if pos >= limit:
+                continue
+            blk, slot = b, pos
+        else:
+            bt = np.asarray(block_table)
+            if pos >= bt.shape[1] * block_size:
+                continue
+            blk, slot = int(bt[b, pos // block_size]), pos % block_size
+        out[blk, slot] = new_rows[b]
+    return out

@@ -209,3 +209,19 @@ def test_binding_rejects_tensors_too_small_for_the_strides():
     with pytest.raises(ValueError):
         K.kv_attn_decode(q, k, k, None, ctx, out, num_kv_heads=2, k_strides=(2 * 8 * 64, 64, 8 * 64),
                          v_strides=(2 * 8 * 64, 64, 8 * 64), block_size=9, num_blocks=2, max_ctx_len=8)
+
+
+def test_append_argument_errors_fail_before_any_hip_call():
+    lib = K._lib
+    p = _params()
+    assert lib.kv_attn_append(None, 16, 16, 16, 16, 16, ctypes.byref(p), None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_append(16, 16, 16, 16, 16, None, ctypes.byref(p), None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_append(16, 16, 16, 16, 16, 16, None, None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_append(8, 16, 16, 16, 16, 16, ctypes.byref(p), None) == K.KV_ATTN_ERR_UNSUPPORTED
+    bad = _params(block_size=24)
+    assert lib.kv_attn_append(16, 16, 16, 16, 16, 16, ctypes.byref(bad), None) == K.KV_ATTN_ERR_SHAPE
+    # append + decode: a missing new row fails before anything else
+    assert lib.kv_attn_append_decode(16, None, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0,
+                                     None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_append_decode(16, 8, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0,
+                                     None) == K.KV_ATTN_ERR_UNSUPPORTED

@@ -269,3 +269,59 @@ def test_numpy_oracle_matches_fsum_at_moderate_length(rng):
     ref = decode_attention(q, k, v, [T])
     alt = np.array(decode_attention_fsum(q.tolist(), k.tolist(), v.tolist(), [T]))
     np.testing.assert_allclose(ref, alt, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# appending the new token's K/V (the step before attention)
+
+
+def test_append_places_rows_exactly_and_nowhere_else(rng):
+    from oracle import append_kv, logical_rows
+    B, hkv, d, bs = 3, 2, 8, 16
+    nblk = 7
+    cache = rng.standard_normal((nblk, bs, hkv, d)).astype(np.float32)
+    table = np.array([[4, 1, 6], [0, 2, 6], [3, 5, 6]])
+    new = rng.standard_normal((B, hkv, d)).astype(np.float32)
+    pos = [17, 0, -1]  # sequence 2 appends nothing
+    out = append_kv(cache, new, pos, table, block_size=bs)
+    changed = np.argwhere(np.any(out != cache, axis=(2, 3)))
+    assert sorted(map(tuple, changed)) == [(0, 0), (1, 1)]  # (block 1, slot 1) and (block 0, slot 0)
+    for b in (0, 1):
+        rows = logical_rows(out, table, b, 0, pos[b] + 1, bs)
+        np.testing.assert_array_equal(rows[pos[b]], new[b, 0].astype(np.float64))
+    assert np.array_equal(cache[3:], out[3:])
+
+
+def test_append_contiguous_and_capacity(rng):
+    from oracle import append_kv
+    cache = np.zeros((2, 10, 1, 4), dtype=np.uint16)
+    new = np.arange(8, dtype=np.uint16).reshape(2, 1, 4) + 1
+    out = append_kv(cache, new, [9, 10], capacity=10)  # position 10 is past the capacity
+    assert np.array_equal(out[0, 9, 0], [1, 2, 3, 4]) and not out[1].any()
+    assert out[0, :9].sum() == 0
+
+
+def test_append_then_attend_equals_attention_over_concatenated_rows(rng):
+    """Appending then attending over T+1 positions is attention over the old rows plus the new
+    one, assembled by hand (independent of the block translation)."""
+    from oracle import append_kv
+    B, hkv, d, bs, T = 1, 1, 16, 16, 20
+    k_old = rng.standard_normal((T, d)).astype(np.float32)
+    v_old = rng.standard_normal((T, d)).astype(np.float32)
+    k_new = rng.standard_normal((B, hkv, d)).astype(np.float32)
+    v_new = rng.standard_normal((B, hkv, d)).astype(np.float32)
+    table = np.array([[2, 0]])
+    kc = np.full((3, bs, hkv, d), np.nan, dtype=np.float32)
+    vc = np.full_like(kc, np.nan)
+    for t in range(T):
+        kc[table[0, t // bs], t % bs, 0] = k_old[t]
+        vc[table[0, t // bs], t % bs, 0] = v_old[t]
+    kc = append_kv(kc, k_new, [T], table, block_size=bs)
+    vc = append_kv(vc, v_new, [T], table, block_size=bs)
+    q = rng.standard_normal((B, 1, d)).astype(np.float32)
+    got = decode_attention(q, kc, vc, [T + 1], table, block_size=bs)
+    keys = np.concatenate([k_old, k_new[0]], axis=0).astype(np.float64)
+    vals = np.concatenate([v_old, v_new[0]], axis=0).astype(np.float64)
+    s = (keys @ q[0, 0].astype(np.float64)) / math.sqrt(d)
+    w = np.exp(s - s.max())
+    np.testing.assert_allclose(got[0, 0], (w @ vals) / w.sum(), rtol=1e-12, atol=1e-14)
