@@ -75,6 +75,11 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
     ap.add_argument("--append", action="store_true",
                     help="each layer first appends the current token's K/V (kv_attn_append_decode)")
+    ap.add_argument("--window", type=int, default=None,
+                    help="sliding window: attend only the last W positions (plus the sinks)")
+    ap.add_argument("--attn-sinks", type=int, default=None,
+                    help="with --window: leading positions always attended (default: the "
+                         "workload's sink count)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run plain device copies of this size (counter calibration runs)")
     return ap.parse_args()
@@ -99,6 +104,17 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     spec = W.PRESETS[args.config]
+    tag = args.config
+    if args.window is not None:
+        if args.window < 1:
+            print("bench.py: --window must be >= 1", file=sys.stderr)
+            sys.exit(2)
+        sinks = spec.num_sinks if args.attn_sinks is None else args.attn_sinks
+        spec = W.preset(args.config, window=args.window, num_sinks=sinks)
+        tag = f"{args.config}_w{args.window}_s{sinks}"
+    elif args.attn_sinks is not None:
+        print("bench.py: --attn-sinks needs --window", file=sys.stderr)
+        sys.exit(2)
     layers = spec.layers
     print(f"[bench] building {args.config} ({layers} layer(s)) on the GPU", file=sys.stderr, flush=True)
     wls = [W.make_workload(spec, device="cuda", layer=l) for l in range(layers)]
@@ -109,9 +125,11 @@ def main():
     plan = calls[0].plan()
     elem = 2 if spec.kv_dtype == "bf16" else 4
     lens = [int(x) for x in wls[0].ctx_lens.cpu().tolist()]
-    kv_bytes_layer = A.unique_kv_read_bytes(lens, spec.num_kv_heads, spec.head_dim, elem)
+    # Algorithmic bytes: the KV of the positions attended (all of them without a window).
+    att = [A.attended_length(t, spec.window, spec.num_sinks) for t in lens]
+    kv_bytes_layer = A.unique_kv_read_bytes(att, spec.num_kv_heads, spec.head_dim, elem)
     kv_bytes_step = kv_bytes_layer * layers
-    flops_step = A.decode_attention_flops(lens, spec.num_q_heads, spec.head_dim) * layers
+    flops_step = A.decode_attention_flops(att, spec.num_q_heads, spec.head_dim) * layers
 
     calib = None
     if args.calib_copy_mib:
@@ -232,10 +250,10 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wls, spec, args.cpu_seconds, elem)
+        cpu = cpu_baseline(wls, spec, args.cpu_seconds, elem, A)
 
     achieved = kv_bytes_layer / (split_us_avg * 1e-6) / 1e9
-    traffic, traffic_src = load_traffic(args.config)
+    traffic, traffic_src = load_traffic(tag)
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -253,9 +271,13 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{spec.name}: {spec.description}",
+            "workload": f"{spec.name}: {spec.description}" + (
+                f"; sliding window of {spec.window} positions plus the first {spec.num_sinks} "
+                "(attention sinks), the rest NaN-poisoned and never read" if spec.window else ""),
             "batch": spec.batch, "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
             "head_dim": spec.head_dim, "max_ctx_len": max(lens), "sum_ctx_len": sum(lens),
+            "window": spec.window, "attn_sinks": spec.num_sinks if spec.window else None,
+            "sum_attended_len": sum(att),
             "layers": layers, "kv_dtype": spec.kv_dtype, "q_dtype": spec.q_dtype,
             "paged": spec.paged, "layout": spec.layout,
             "unique_kv_bytes_per_step": kv_bytes_step, "flops_per_step": flops_step,
@@ -296,7 +318,7 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wls, spec, budget_s, elem):
+def cpu_baseline(wls, spec, budget_s, elem, A):
     """The oracle, as it stands, on whole (layer, sequence, KV head) units of the workload, in
     order, until the time budget is spent (at least one unit). Host copies of each unit are made
     outside the timed region. Returns the oracle's unique-KV GB/s."""
@@ -311,9 +333,10 @@ def cpu_baseline(wls, spec, budget_s, elem):
         v = W.oracle_sample(wls[l], [b], [h])
         t0 = time.perf_counter()
         decode_attention(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
-                         block_size=v["block_size"] if v["block_table"] is not None else None)
+                         block_size=v["block_size"] if v["block_table"] is not None else None,
+                         window=spec.window, num_sinks=spec.num_sinks)
         spent += time.perf_counter() - t0
-        done_bytes += 2 * int(lens[l][b]) * spec.head_dim * elem
+        done_bytes += 2 * A.attended_length(lens[l][b], spec.window, spec.num_sinks) * spec.head_dim * elem
         n += 1
         if spent >= budget_s:
             break

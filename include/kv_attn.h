@@ -30,9 +30,16 @@
  * - Entry points are thread-safe: the only shared state is a per-device cache of the compute
  *   unit count, filled once.
  * - GQA grouping: with g = num_q_heads / num_kv_heads, query head h reads KV head h / g.
- * - ctx_lens[b] counts every position attended, the current token included (the caller has
- *   already appended it); there is no mask inside those positions. ctx_lens[b] == 0 gives an
- *   output row of zeros.
+ * - ctx_lens[b] counts every position in the cache, the current token included (the caller has
+ *   already appended it). Without a window every one of them is attended; ctx_lens[b] == 0
+ *   gives an output row of zeros.
+ * - Sliding window with attention sinks (params.window > 0): a sequence of length T attends
+ *   only to its first min(num_sinks, T) positions and its last min(window, T) positions, each
+ *   position once. Ch. 19 §19.4.3 bounds the cache of a long sequence by keeping only a recent
+ *   window of tokens, and keeping the first few tokens as well (StreamingLLM's attention sinks)
+ *   keeps the softmax stable; the positions outside the two ranges are neither read nor
+ *   attended. The split kernel enumerates only the tiles of 16 positions that hold attended
+ *   positions, so a step's HBM traffic follows the attended positions, not T.
  */
 #ifndef KV_ATTN_H_
 #define KV_ATTN_H_
@@ -44,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KV_ATTN_ABI_VERSION 1
+#define KV_ATTN_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum kv_attn_status {
@@ -94,10 +101,14 @@ typedef struct kv_attn_params {
   int32_t q_dtype;            /* kv_attn_dtype */
   int32_t kv_dtype;           /* kv_attn_dtype */
   float scale;                /* score scale; 0 means 1/sqrt(head_dim) */
-  int32_t reserved;           /* must be 0 */
+  int32_t window;             /* 0 = attend every position; > 0 = sliding window of this many
+                                 positions (plus the sinks), see the conventions above */
   int64_t num_blocks;         /* physical blocks in the caches (contiguous: batch); validator bound */
   int64_t k_stride_block, k_stride_token, k_stride_head; /* elements, >= 0 */
   int64_t v_stride_block, v_stride_token, v_stride_head; /* elements, >= 0 */
+  int32_t num_sinks;          /* >= 0; leading positions attended as well when window > 0
+                                 (ignored when window == 0) */
+  int32_t reserved;           /* must be 0 */
 } kv_attn_params;
 
 /* The launch plan kv_attn_decode will use for a problem (split planning). */
@@ -125,7 +136,9 @@ const char* kv_attn_status_string(int32_t status);
  * current HIP device). Validates `p` exactly as kv_attn_decode does (pointers aside). Split
  * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
  * workgroups number at least about one per compute unit, each split spans 16..256 tiles, and a
- * caller-given num_splits overrides the count. Writes *plan only on KV_ATTN_OK.
+ * caller-given num_splits overrides the count. With a window the tiles counted are those a
+ * sequence can visit: ceil(min(num_sinks, max_ctx_len) / 16) + ceil(window / 16) + 1 at most.
+ * Writes *plan only on KV_ATTN_OK.
  */
 kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_attn_plan* plan);
 
@@ -163,9 +176,13 @@ kv_attn_status kv_attn_decode(const void* q, const void* k_cache, const void* v_
  * unnormalised sums O at byte offset 0 as fp32 [batch * num_q_heads, S, head_dim] and (m, l) at
  * byte offset plan.ml_offset as fp32 [batch * num_q_heads, S, 2], m being a base-2 maximum (see
  * kv_attn_merge). Split s of sequence b covers positions [s * split_len, (s+1) * split_len) of
- * that sequence; splits starting at or past ctx_lens[b] are not written.
+ * that sequence; splits starting at or past ctx_lens[b] are not written. With a window the
+ * split covers the same number of 16-position tiles, counted over the visited tiles only (the
+ * sink tiles first, then the window's), so that ceil(n_b / (split_len / 16)) splits are written,
+ * n_b being the sequence's visited tiles.
  * kv_attn_decode_merge: the merge pass over a workspace the split pass filled; it merges, for
- * row (b, h), the first ceil(ctx_lens[b] / split_len) splits into out.
+ * row (b, h), the first ceil(ctx_lens[b] / split_len) splits into out (with a window, the
+ * splits the split pass wrote).
  */
 kv_attn_status kv_attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
                                     const int32_t* block_table, const int32_t* ctx_lens, float* out,

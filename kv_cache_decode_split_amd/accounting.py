@@ -28,6 +28,7 @@ from __future__ import annotations
 from typing import Iterable, Union
 
 __all__ = [
+    "attended_length",
     "MI355X_HBM_PEAK_GBPS",
     "kv_cache_bytes_eq3",
     "kv_bytes_per_token",
@@ -70,6 +71,16 @@ def kv_bytes_per_token(num_layers: int, hidden: int, elem_bytes: int = 2) -> int
 def unique_kv_bytes_per_position(num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """Bytes of K and V for one (sequence, position) over all KV heads: 2 · d_kv · b_kv."""
     return 2 * num_kv_heads * head_dim * elem_bytes
+
+
+def attended_length(length: int, window: int | None = None, num_sinks: int = 0) -> int:
+    """Positions a decode step attends to in a sequence of ``length`` positions: all of them, or
+    with a window W the union of the first ``num_sinks`` and the last W positions (Ch. 19 §19.4.3
+    sliding window with attention sinks). These are the positions whose KV the step reads."""
+    length = max(int(length), 0)
+    if window is None:
+        return length
+    return min(length, min(int(num_sinks), length) + min(int(window), length))
 
 
 def unique_kv_read_bytes(lengths: Lengths, num_kv_heads: int, head_dim: int, elem_bytes: int,

@@ -208,6 +208,8 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.max_ctx = p->max_ctx_len;
     a.split_tiles = plan.split_tiles;
     a.num_splits = plan.num_splits;
+    a.window = p->window;
+    a.num_sinks = p->num_sinks;
     const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
     a.scale_log2 = float(scale * 1.4426950408889634);  // log2(e)
     if (launch_split(a, plan, p->head_dim, paged, p->q_dtype == KV_ATTN_BF16,
@@ -224,8 +226,10 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     m.rows = p->batch * p->num_q_heads;
     m.num_splits = plan.num_splits;
     m.h_q = p->num_q_heads;
-    m.split_len = plan.split_tiles * kTile;
+    m.split_tiles = plan.split_tiles;
     m.max_ctx = p->max_ctx_len;
+    m.window = p->window;
+    m.num_sinks = p->num_sinks;
     if (launch_merge(m, p->head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
   }
   if (debug_mode()) {
@@ -310,8 +314,10 @@ kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
   m.rows = rows;
   m.num_splits = num_splits;
   m.h_q = 1;
-  m.split_len = 1;
+  m.split_tiles = 1;
   m.max_ctx = 0;
+  m.window = 0;
+  m.num_sinks = 0;
   if (kvattn::launch_merge(m, head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
   if (kvattn::debug_mode()) {
     if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess ||

@@ -45,6 +45,8 @@ struct SplitArgs {
   int32_t split_tiles;         // tiles per split
   int32_t num_splits;          // S
   float scale_log2;            // scale * log2(e)
+  int32_t window;              // > 0: attend only the last `window` positions plus the sinks
+  int32_t num_sinks;           // leading positions always attended when a window is set
 };
 
 struct MergeArgs {
@@ -56,8 +58,10 @@ struct MergeArgs {
   int32_t rows;
   int32_t num_splits;
   int32_t h_q;                 // decode path: row / h_q is the sequence
-  int32_t split_len;           // decode path
+  int32_t split_tiles;         // decode path: tiles per split
   int32_t max_ctx;             // decode path: clamp of ctx_lens
+  int32_t window;              // decode path: as in SplitArgs
+  int32_t num_sinks;
 };
 
 // Everything the append kernel needs: one new K/V row per (sequence, KV head) is stored at

@@ -208,7 +208,18 @@ void split_kernel(const SplitArgs a) {
 
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int ntiles = (ctx + kTile - 1) / kTile;
+  // Attended positions: all of [0, ctx), or with a window W the sinks [0, sink_end) and the
+  // recent positions [win_start, ctx). Their tiles are enumerated as "virtual" tiles: the
+  // n_first tiles of the sink range, then the tiles from win_tile0 to the last tile (a tile is
+  // never visited twice when the two ranges meet). Without a window sink_end = win_start = 0.
+  int sink_end = 0, win_start = 0, n_first = 0, win_tile0 = 0;
+  if (a.window > 0) {
+    sink_end = min(a.num_sinks, ctx);
+    win_start = max(ctx - a.window, 0);
+    n_first = (sink_end + kTile - 1) / kTile;
+    win_tile0 = max(win_start / kTile, n_first);
+  }
+  const int ntiles = n_first + max((ctx + kTile - 1) / kTile - win_tile0, 0);
   const int t_begin = split * a.split_tiles;
   const int64_t q_row0 = int64_t(b) * a.h_q + int64_t(kvh) * g;  // first query head of the group
   if (t_begin >= ntiles) {
@@ -265,9 +276,10 @@ void split_kernel(const SplitArgs a) {
 
   // ---- tile addressing -------------------------------------------------------------------------
   // A tile's rows sit at a uniform base (scalar arithmetic) plus per-lane 32-bit byte offsets
-  // that are the same for every full tile. Only the last, partial tile of a sequence recomputes
-  // them, with the row index clamped to its last valid row, so no lane ever addresses a
-  // position at or past the sequence length.
+  // that are the same for every tile whose 16 positions are all attended. A partial tile (the
+  // sequence's last tile, or a tile at an edge of the sink or window range) recomputes them
+  // with every unattended row redirected to an attended row of the same tile, so no lane ever
+  // addresses a position that is not attended (such rows are masked out of the scores).
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
   const int64_t k_head = int64_t(kvh) * a.k_sh;
@@ -277,18 +289,28 @@ void split_kernel(const SplitArgs a) {
     int kr[4];    // variant 0: key rows 4*q4+i, elements r16*EPL
     int v[4];     // value rows 4*q4+i, elements r16*EPL
   };
-  auto lane_offsets = [&](int last) __attribute__((always_inline)) {
+  // Tile row m (position p0 + m) is attended iff it lies below ctx and is a sink or in the window.
+  auto attended_at = [&](int p0, int m) __attribute__((always_inline)) {
+    const int pos = p0 + m;
+    return pos < ctx && (pos < sink_end || pos >= win_start);
+  };
+  // row_of(m) is the row a lane loads for tile row m.
+  auto lane_offsets = [&](auto row_of) __attribute__((always_inline)) {
     LaneOffsets o;
-    o.k = (min(r16, last) * int(a.k_st) + q4 * 8) * KVB;
+    o.k = (row_of(r16) * int(a.k_st) + q4 * 8) * KVB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = min(4 * q4 + i, last);
+      const int row = row_of(4 * q4 + i);
       o.kr[i] = (row * int(a.k_st) + r16 * EPL) * KVB;
       o.v[i] = (row * int(a.v_st) + r16 * EPL) * KVB;
     }
     return o;
   };
-  const LaneOffsets full = lane_offsets(kTile - 1);
+  const LaneOffsets full = lane_offsets([](int m) { return m; });
+
+  auto logical_tile = [&](int vt) __attribute__((always_inline)) {
+    return vt < n_first ? vt : win_tile0 + (vt - n_first);
+  };
 
   // Paged caches: the block ids of this wave's tiles k0 .. k0+63 sit one per lane in bt_vec and
   // are read with a (scalar) lane read. Consuming the register right after it is loaded makes the
@@ -298,7 +320,7 @@ void split_kernel(const SplitArgs a) {
     const int kk = k0 + lane;
     int blk = 0;
     if (kk < n_w)
-      blk = a.block_table[int64_t(b) * a.max_blocks + (((first + kWaves * kk) * kTile) >> a.bs_log2)];
+      blk = a.block_table[int64_t(b) * a.max_blocks + ((logical_tile(first + kWaves * kk) * kTile) >> a.bs_log2)];
     bt_vec = blk;
     bt_base = k0;
     asm volatile("" ::"v"(bt_vec));
@@ -311,9 +333,8 @@ void split_kernel(const SplitArgs a) {
   };
 
   auto load_tile = [&](int k, Frag& f) __attribute__((always_inline)) {
-    const int tile = first + kWaves * k;
+    const int tile = logical_tile(first + kWaves * k);
     const int p0 = tile * kTile;
-    const int last = ctx - 1 - p0;  // >= 0; rows past it are clamped to it
     int64_t koff, voff;             // element offset of tile row 0
     if (paged) {
       if (k - bt_base >= 64) fetch_block_ids(k & ~63);
@@ -327,7 +348,13 @@ void split_kernel(const SplitArgs a) {
     }
     const char* kt = kbase + koff * KVB;
     const char* vt = vbase + voff * KVB;
-    const LaneOffsets o = last >= kTile - 1 ? full : lane_offsets(last);
+    // Every visited tile holds at least one attended row: row 0 if it is a sink row, else the
+    // first row at or past the window start.
+    const bool whole = p0 + kTile <= ctx && (p0 + kTile <= sink_end || p0 >= win_start);
+    const int anchor = p0 < sink_end ? 0 : max(win_start - p0, 0);
+    const LaneOffsets o = whole ? full : lane_offsets([&](int m) __attribute__((always_inline)) {
+      return attended_at(p0, m) ? m : anchor;
+    });
     if constexpr (MFMA) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) f.kc[c] = load_stream16(kt + o.k + c * 64);
@@ -340,8 +367,8 @@ void split_kernel(const SplitArgs a) {
   };
 
   auto compute_tile = [&](int k, const Frag& f) __attribute__((always_inline)) {
-    const int tile = first + kWaves * k;
-    const int nvalid = ctx - tile * kTile;  // positions 0 .. nvalid-1 of the tile are real
+    const int p0 = logical_tile(first + kWaves * k) * kTile;
+    auto attended = [&](int m) __attribute__((always_inline)) { return attended_at(p0, m); };
     float p[4][G];                          // variant 0: probabilities of rows 4*q4+i
     float pm[4];                            // variant 1: probability of (row 4*q4+i, head r16)
     bool rescale;
@@ -354,7 +381,7 @@ void split_kernel(const SplitArgs a) {
       // acc[r] = score of tile row 4*q4 + r for head r16.
       float s[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[r] = (4 * q4 + r < nvalid) ? acc[r] * a.scale_log2 : neg_inf();
+      for (int r = 0; r < 4; ++r) s[r] = attended(4 * q4 + r) ? acc[r] * a.scale_log2 : neg_inf();
       float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mt = max_xor32(max_xor16(mt));
       const float m_new = fmaxf(m_run, mt);
@@ -377,7 +404,7 @@ void split_kernel(const SplitArgs a) {
       for (int i = 0; i < 4; ++i) {
         float kf[EPL];
         widen<EPL, KV_BF16>(f.kr[i], kf);
-        const bool valid = 4 * q4 + i < nvalid;
+        const bool valid = attended(4 * q4 + i);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           float x = 0.f;
@@ -563,9 +590,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
   if (a.num_valid != nullptr) {
     nv = a.num_valid[row];
   } else if (a.ctx_lens != nullptr) {
+    // Same tile enumeration as the split kernel: splits past the sequence's tiles hold nothing.
     int ctx = a.ctx_lens[row / a.h_q];
     ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-    nv = (ctx + a.split_len - 1) / a.split_len;
+    int n_first = 0, win_tile0 = 0;
+    if (a.window > 0) {
+      n_first = (min(a.num_sinks, ctx) + kTile - 1) / kTile;
+      win_tile0 = max(max(ctx - a.window, 0) / kTile, n_first);
+    }
+    const int ntiles = n_first + max((ctx + kTile - 1) / kTile - win_tile0, 0);
+    nv = (ntiles + a.split_tiles - 1) / a.split_tiles;
   }
   nv = nv < 0 ? 0 : (nv > S ? S : nv);
   const float* ml = a.ml_part + int64_t(row) * S * 2;

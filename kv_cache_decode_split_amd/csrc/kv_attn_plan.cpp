@@ -41,6 +41,7 @@ kv_attn_status validate_params(const kv_attn_params* p) {
     return KV_ATTN_ERR_UNSUPPORTED;
   if (p->reserved != 0) return KV_ATTN_ERR_VALUE;
   if (p->max_ctx_len < 0 || p->num_splits < 0) return KV_ATTN_ERR_VALUE;
+  if (p->window < 0 || p->num_sinks < 0) return KV_ATTN_ERR_VALUE;
   if (!isfinite(p->scale)) return KV_ATTN_ERR_VALUE;
   if (p->block_size < 1 || p->num_blocks < 1) return KV_ATTN_ERR_SHAPE;
   const int64_t strides[6] = {p->k_stride_block, p->k_stride_token, p->k_stride_head,
@@ -74,15 +75,26 @@ kv_attn_status validate_layout(const kv_attn_params* p, bool paged) {
   return KV_ATTN_OK;
 }
 
-// Split planning. The positions of one (sequence, KV head) pair are cut into tiles of kTile,
-// and the tiles into S splits of split_tiles tiles; every split is one workgroup of kWaves
-// waves. The grid is sized from the host-known max_ctx_len: workgroups whose split starts past
-// their own sequence's length exit at once, so ragged batches need no host copy of ctx_lens.
+// Tiles of kTile positions a sequence of at most max_ctx_len positions can visit. With a
+// window W and n sinks that is at most ceil(min(n, T)/16) sink tiles plus the ceil(W/16) + 1
+// tiles that W consecutive positions can touch, and never more than the whole sequence's tiles.
+int64_t max_visited_tiles(const kv_attn_params* p) {
+  const int64_t all = ceil_div(p->max_ctx_len > 0 ? p->max_ctx_len : 1, kTile);
+  if (p->window <= 0) return all;
+  const int64_t sinks = p->num_sinks < p->max_ctx_len ? p->num_sinks : p->max_ctx_len;
+  const int64_t bounded = ceil_div(sinks, kTile) + ceil_div(p->window, kTile) + 1;
+  return bounded < all ? bounded : all;
+}
+
+// Split planning. The visited tiles of one (sequence, KV head) pair are cut into S splits of
+// split_tiles tiles; every split is one workgroup of kWaves waves. The grid is sized from the
+// host-known max_ctx_len: workgroups whose split starts past their own sequence's tiles exit at
+// once, so ragged batches need no host copy of ctx_lens.
 kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   const kv_attn_status st = validate_params(p);
   if (st != KV_ATTN_OK) return st;
   if (num_cus < 1) return KV_ATTN_ERR_VALUE;
-  const int64_t tiles_max = ceil_div(p->max_ctx_len > 0 ? p->max_ctx_len : 1, kTile);
+  const int64_t tiles_max = max_visited_tiles(p);
   const int64_t units = int64_t(p->batch) * p->num_kv_heads;
   int64_t S;
   if (p->num_splits > 0) {

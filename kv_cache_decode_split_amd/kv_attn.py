@@ -89,7 +89,7 @@ class kv_attn_params(ctypes.Structure):
         ("q_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("window", ctypes.c_int32),
         ("num_blocks", ctypes.c_int64),
         ("k_stride_block", ctypes.c_int64),
         ("k_stride_token", ctypes.c_int64),
@@ -97,6 +97,8 @@ class kv_attn_params(ctypes.Structure):
         ("v_stride_block", ctypes.c_int64),
         ("v_stride_token", ctypes.c_int64),
         ("v_stride_head", ctypes.c_int64),
+        ("num_sinks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -171,12 +173,21 @@ def make_params(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: in
                 k_strides: Sequence[int], v_strides: Sequence[int],
                 max_blocks_per_seq: int = 1, num_splits: int = 0,
                 q_dtype: int = KV_ATTN_BF16, kv_dtype: int = KV_ATTN_BF16,
-                scale: float = 0.0) -> kv_attn_params:
-    """Fill a ``kv_attn_params`` (strides are (block, token, head) in elements)."""
+                scale: float = 0.0, window: Optional[int] = None,
+                num_sinks: int = 0) -> kv_attn_params:
+    """Fill a ``kv_attn_params`` (strides are (block, token, head) in elements).
+
+    ``window=None`` attends every position; an integer W >= 1 attends the last W positions of
+    each sequence plus its first ``num_sinks`` positions.
+    """
+    if window is not None and int(window) < 1:
+        raise ValueError("window must be None (no window) or >= 1")
     p = kv_attn_params()
     p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = batch, num_q_heads, num_kv_heads, head_dim
     p.block_size, p.max_blocks_per_seq, p.max_ctx_len = block_size, max_blocks_per_seq, max_ctx_len
     p.num_splits, p.q_dtype, p.kv_dtype, p.scale, p.reserved = num_splits, q_dtype, kv_dtype, scale, 0
+    p.window = 0 if window is None else int(window)
+    p.num_sinks = int(num_sinks)
     p.num_blocks = num_blocks
     p.k_stride_block, p.k_stride_token, p.k_stride_head = (int(s) for s in k_strides)
     p.v_stride_block, p.v_stride_token, p.v_stride_head = (int(s) for s in v_strides)
@@ -223,13 +234,15 @@ class DecodeCall:
     is at block*strides[0] + token*strides[1] + head*strides[2] + i. block_table: int32
     [B, max_blocks] (paged; block_size tokens per block) or None (contiguous; block_size = slot
     capacity). ctx_lens: int32 [B] on the device. max_ctx_len defaults to ctx_lens.max() (a host
-    sync). The workspace, if not given, is allocated once from torch's allocator.
+    sync). The workspace, if not given, is allocated once from torch's allocator. ``window`` /
+    ``num_sinks`` restrict attention to the first num_sinks and last window positions.
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, ctx_lens, out, *, num_kv_heads: int,
                  k_strides: Sequence[int], v_strides: Sequence[int], block_size: int,
                  num_blocks: int, max_ctx_len: Optional[int] = None, scale: float = 0.0,
-                 num_splits: int = 0, workspace: Optional[torch.Tensor] = None):
+                 num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
+                 window: Optional[int] = None, num_sinks: int = 0):
         if q.dim() != 3 or not q.is_contiguous():
             raise ValueError("q must be a contiguous [B, h_q, d] tensor")
         B, hq, d = q.shape
@@ -259,7 +272,8 @@ class DecodeCall:
             batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=block_size,
             max_ctx_len=int(max_ctx_len), num_blocks=num_blocks, k_strides=k_strides,
             v_strides=v_strides, max_blocks_per_seq=max_blocks, num_splits=num_splits,
-            q_dtype=_dtype_code(q.dtype), kv_dtype=_dtype_code(k_cache.dtype), scale=float(scale))
+            q_dtype=_dtype_code(q.dtype), kv_dtype=_dtype_code(k_cache.dtype), scale=float(scale),
+            window=window, num_sinks=num_sinks)
         _check_extent(k_cache, k_strides, num_blocks, block_size, hkv, d, "k_cache")
         _check_extent(v_cache, v_strides, num_blocks, block_size, hkv, d, "v_cache")
         ws_bytes = kv_attn_workspace_size(self.params)
@@ -371,8 +385,11 @@ def kv_attn_append_decode(q, k_new, v_new, k_cache, v_cache, block_table, ctx_le
 
 def _workload_args(w) -> dict:
     ks, vs = w.kv_strides()
-    return dict(num_kv_heads=w.spec.num_kv_heads, k_strides=ks, v_strides=vs,
+    args = dict(num_kv_heads=w.spec.num_kv_heads, k_strides=ks, v_strides=vs,
                 block_size=w.block_size, num_blocks=w.num_blocks, max_ctx_len=w.max_ctx_len)
+    if getattr(w.spec, "window", None) is not None:
+        args.update(window=w.spec.window, num_sinks=w.spec.num_sinks)
+    return args
 
 
 def kv_attn_decode_workload(w, out: torch.Tensor, *, stream=None, **kwargs) -> None:

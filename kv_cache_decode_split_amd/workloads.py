@@ -72,6 +72,9 @@ class WorkloadSpec:
     layers: int = 1
     extra_blocks: int = 1           # paged: unused (NaN) physical blocks, at least 1
     capacity: Optional[int] = None  # contiguous: tokens per sequence slot (default max ctx)
+    # Sliding window: None attends every position; W >= 1 attends only the first num_sinks and
+    # the last W positions of each sequence, and every other position is NaN-poisoned.
+    window: Optional[int] = None
     description: str = ""
 
     @property
@@ -263,11 +266,43 @@ def make_workload(spec: WorkloadSpec, device="cpu", layer: int = 0) -> Workload:
     for blk in st["unused_blocks"]:
         kv[blk].fill_(nan)
         vv[blk].fill_(nan)
+    if spec.window is not None:
+        _poison_outside_window(k, v, kv, vv, spec, ctx_list, table, block_size)
 
     ctx_dev = ctx.to(device)
     table_dev = table.to(device) if table is not None else None
     return Workload(spec=spec, q=q, k_cache=k, v_cache=v, block_table=table_dev, ctx_lens=ctx_dev,
                     block_size=block_size, num_blocks=num_blocks, layer=layer)
+
+
+def _poison_outside_window(k, v, kv, vv, spec, ctx_list, table, block_size) -> None:
+    """NaN into every position of a windowed sequence that is neither one of its first
+    ``num_sinks`` positions nor one of its last ``window`` positions. Whole blocks of such
+    positions are filled with one indexed fill; the (at most two) blocks cut by an edge slot by
+    slot range."""
+    nan = float("nan")
+    whole = []
+    for b, length in enumerate(ctx_list):
+        lo, hi = min(spec.num_sinks, length), max(length - spec.window, 0)  # gap [lo, hi)
+        if hi <= lo:
+            continue
+        if table is None:
+            kv[b, lo:hi].fill_(nan)
+            vv[b, lo:hi].fill_(nan)
+            continue
+        for j in range(lo // block_size, (hi + block_size - 1) // block_size):
+            start = j * block_size
+            a, e = max(lo, start), min(hi, start + block_size)
+            blk = int(table[b, j])
+            if a == start and e == start + block_size:
+                whole.append(blk)
+            else:
+                kv[blk, a - start:e - start].fill_(nan)
+                vv[blk, a - start:e - start].fill_(nan)
+    if whole:
+        idx = torch.tensor(whole, dtype=torch.int64, device=k.device)
+        k.index_fill_(0, idx, nan)  # axis 0 is the physical block in both layouts
+        v.index_fill_(0, idx, nan)
 
 
 def _np_storage(t: torch.Tensor) -> np.ndarray:

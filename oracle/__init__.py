@@ -27,6 +27,7 @@ brute force and the independent pure-Python implementation (no function is "pari
 from .decode_attention import (  # noqa: F401
     widen,
     logical_rows,
+    attended_positions,
     stable_softmax,
     attend_one,
     decode_attention,

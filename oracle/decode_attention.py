@@ -23,6 +23,9 @@ Readings taken where the pages leave a point open (each is also listed in DESIGN
 * ``ctx_lens[b]`` counts every position to attend, the current token included (the cache was
   appended before the step); there is no mask inside those positions.
 * ``ctx_lens[b] == 0`` yields a zero output row (softmax of an empty set is undefined).
+* Window / sinks (Ch. 19 §19.4.3 describes keeping only the last W tokens, and StreamingLLM's
+  first "sink" tokens plus a recent window): with a window W the attended positions are the
+  first ``num_sinks`` positions and the last W positions of the sequence, each once.
 * Cache arrays are indexed ``[block, slot, kv_head, dim]``. Contiguous caches are the case with
   no block table: sequence ``b`` is block ``b`` and logical position ``t`` is slot ``t``.
 * Storage types: ``float32`` arrays hold fp32 values; ``uint16`` arrays hold bf16 bit patterns.
@@ -39,6 +42,7 @@ import numpy as np
 __all__ = [
     "widen",
     "logical_rows",
+    "attended_positions",
     "stable_softmax",
     "attend_one",
     "decode_attention",
@@ -103,9 +107,23 @@ def attend_one(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float
     return probs @ values
 
 
+def attended_positions(length: int, window: int | None = None, num_sinks: int = 0) -> np.ndarray:
+    """Positions a decode step attends to among ``0 .. length-1``.
+
+    Without a window: all of them. With a window W (Ch. 19 §19.4.3: a sliding window keeps the
+    last W tokens; StreamingLLM additionally keeps the first tokens, the attention sinks): the
+    first ``num_sinks`` positions and the last W positions, each position once.
+    """
+    t = np.arange(length, dtype=np.int64)
+    if window is None:
+        return t
+    return t[(t < num_sinks) | (t >= length - window)]
+
+
 def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, ctx_lens,
                      block_table=None, *, block_size: int | None = None,
-                     scale: float | None = None) -> np.ndarray:
+                     scale: float | None = None, window: int | None = None,
+                     num_sinks: int = 0) -> np.ndarray:
     """Decode attention for a batch of sequences, one new query token per sequence.
 
     Parameters
@@ -117,6 +135,7 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, ct
     block_table : [B, max_blocks] integers or ``None``.
     block_size : tokens per block for a paged cache.
     scale : score scale; ``None`` means 1/√d (Ch. 19 §19.4.1).
+    window, num_sinks : restrict attention to :func:`attended_positions` (``None``: all).
 
     Returns
     -------
@@ -139,9 +158,10 @@ def decode_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, ct
         length = int(ctx[b])
         if length <= 0:
             continue
+        keep = attended_positions(length, window, num_sinks)
         for kvh in range(h_kv):
-            keys = logical_rows(k_cache, block_table, b, kvh, length, block_size)
-            values = logical_rows(v_cache, block_table, b, kvh, length, block_size)
+            keys = logical_rows(k_cache, block_table, b, kvh, length, block_size)[keep]
+            values = logical_rows(v_cache, block_table, b, kvh, length, block_size)[keep]
             for j in range(group):
                 h = kvh * group + j
                 out[b, h] = attend_one(qf[b, h], keys, values, scale)

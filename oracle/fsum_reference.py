@@ -25,8 +25,9 @@ def _value(raw, is_bf16: bool) -> float:
 
 
 def decode_attention_fsum(q, k_cache, v_cache, ctx_lens, block_table=None, *,
-                          block_size=None, scale=None, bf16=False):
-    """Same contract as ``oracle.decode_attention.decode_attention``; returns nested lists.
+                          block_size=None, scale=None, bf16=False, window=None, num_sinks=0):
+    """Same contract as ``oracle.decode_attention.decode_attention`` (window and sinks included);
+    returns nested lists.
 
     ``q`` is indexable as q[b][h][i]; caches as cache[block][slot][kv_head][i]. With
     ``bf16=True`` every stored element is a bf16 bit pattern.
@@ -48,6 +49,8 @@ def decode_attention_fsum(q, k_cache, v_cache, ctx_lens, block_table=None, *,
             qv = [_value(q[b][h][i], bf16) for i in range(d)]
             rows = []
             for t in range(length):
+                if window is not None and not (t < num_sinks or t >= length - window):
+                    continue
                 if block_table is None:
                     blk, slot = b, t
                 else:

@@ -45,12 +45,19 @@ def run(w: W.Workload, **kwargs) -> torch.Tensor:
     return out
 
 
+def _window_kwargs(w: W.Workload) -> dict:
+    """The workload's sliding window, in the oracle's terms (None = every position)."""
+    if w.spec.window is None:
+        return {}
+    return dict(window=w.spec.window, num_sinks=w.spec.num_sinks)
+
+
 def oracle_full(w: W.Workload, scale=None) -> np.ndarray:
     from oracle import decode_attention
     v = W.oracle_view(w)
     return decode_attention(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
                             block_size=v["block_size"] if v["block_table"] is not None else None,
-                            scale=scale)
+                            scale=scale, **_window_kwargs(w))
 
 
 def oracle_rows(w: W.Workload, seqs, kv_heads=None, scale=None) -> np.ndarray:
@@ -59,7 +66,7 @@ def oracle_rows(w: W.Workload, seqs, kv_heads=None, scale=None) -> np.ndarray:
     v = W.oracle_sample(w, seqs, kv_heads)
     return decode_attention(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
                             block_size=v["block_size"] if v["block_table"] is not None else None,
-                            scale=scale)
+                            scale=scale, **_window_kwargs(w))
 
 
 def select_rows(out: torch.Tensor, w: W.Workload, seqs, kv_heads=None) -> np.ndarray:

@@ -61,7 +61,7 @@ def test_struct_layout_matches_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert K.kv_attn_abi_version() == 1
+    assert K.kv_attn_abi_version() == 2
     for code in range(8):
         s = K.kv_attn_status_string(code)
         assert s and s != "unknown status"
@@ -88,12 +88,48 @@ def _params(**kw):
     (dict(num_splits=-2), K.KV_ATTN_ERR_VALUE),
     (dict(scale=float("nan")), K.KV_ATTN_ERR_VALUE),
     (dict(num_blocks=0), K.KV_ATTN_ERR_SHAPE),
+    (dict(window=64, num_sinks=-1), K.KV_ATTN_ERR_VALUE),
 ])
 def test_get_plan_rejects_invalid_params(kw, status):
     p = _params(**kw)
     with pytest.raises(K.KvAttnError) as e:
         K.kv_attn_get_plan(p, 256)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("field,value", [("window", -1), ("reserved", 1)])
+def test_get_plan_rejects_raw_field_values(field, value):
+    """Fields the binding never sets this way are still checked by the library."""
+    p = _params()
+    setattr(p, field, value)
+    with pytest.raises(K.KvAttnError) as e:
+        K.kv_attn_get_plan(p, 256)
+    assert e.value.status == K.KV_ATTN_ERR_VALUE
+
+
+def test_binding_rejects_a_window_below_one():
+    with pytest.raises(ValueError):
+        _params(window=0)
+
+
+@pytest.mark.parametrize("T,W,n", [(131072, 4096, 4), (131072, 1, 0), (131072, 4095, 17),
+                                   (5000, 8192, 4), (100, 7, 200), (32768, 256, 0)])
+def test_window_plan_sizes_the_grid_by_the_visited_tiles(T, W, n):
+    """With a window the split grid covers the visited tiles of a sequence: at most the sink
+    tiles plus the ceil(W/16) + 1 tiles the window touches, never more than the whole sequence."""
+    p = _params(batch=4, num_q_heads=64, num_kv_heads=8, max_ctx_len=T,
+                max_blocks_per_seq=(T + 15) // 16, num_blocks=10**6, window=W, num_sinks=n)
+    plan = K.kv_attn_get_plan(p, 256)
+    bound = min((T + 15) // 16, (min(n, T) + 15) // 16 + (W + 15) // 16 + 1)
+    # The largest visited-tile count any length t <= T gives, enumerated directly.
+    worst = 0
+    for t in range(max(0, T - 64), T + 1):
+        s_end, w0 = min(n, t), max(t - W, 0)
+        tiles = {p // 16 for p in range(t) if p < s_end or p >= w0}
+        worst = max(worst, len(tiles))
+    assert worst <= bound
+    S, L = plan["num_splits"], plan["split_len"]
+    assert S * (L // 16) >= bound and (S - 1) * (L // 16) < bound
 
 
 def test_plan_covers_every_tile_and_respects_bounds():

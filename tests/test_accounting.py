@@ -108,3 +108,14 @@ def test_workload_byte_counts():
 def test_roofline_sum():
     ks = [(0.0, 8e9, 1.0, 8e12), (1e9, 0.0, 1e12, 1.0)]
     assert A.roofline_time_sum(ks, exposed_other=1e-6) == pytest.approx(1e-3 + 1e-3 + 1e-6)
+
+
+def test_attended_length_counts_the_oracle_positions():
+    """The bench's byte count under a window equals the number of positions the oracle attends."""
+    from oracle import attended_positions
+    for length in (0, 1, 5, 16, 17, 100, 4096):
+        assert A.attended_length(length) == length
+        for window in (1, 3, 16, 64, 5000):
+            for sinks in (0, 1, 4, 50, 10000):
+                want = len(attended_positions(length, window, sinks))
+                assert A.attended_length(length, window, sinks) == want, (length, window, sinks)

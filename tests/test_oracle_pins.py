@@ -325,3 +325,58 @@ def test_append_then_attend_equals_attention_over_concatenated_rows(rng):
     s = (keys @ q[0, 0].astype(np.float64)) / math.sqrt(d)
     w = np.exp(s - s.max())
     np.testing.assert_allclose(got[0, 0], (w @ vals) / w.sum(), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# sliding window and attention sinks (Ch. 19 §19.4.3)
+
+
+def test_attended_positions_sets():
+    from oracle import attended_positions
+    assert attended_positions(10).tolist() == list(range(10))
+    assert attended_positions(10, 3).tolist() == [7, 8, 9]
+    assert attended_positions(10, 3, 2).tolist() == [0, 1, 7, 8, 9]
+    assert attended_positions(10, 8, 4).tolist() == list(range(10))      # overlap: each once
+    assert attended_positions(3, 5, 4).tolist() == [0, 1, 2]
+    assert attended_positions(10, 0, 2).tolist() == [0, 1]
+    assert attended_positions(0, 4, 4).tolist() == []
+
+
+def test_window_of_one_returns_the_last_value_row(rng):
+    k, v = _contig(rng, 2, 2, 30, 8)
+    q = rng.standard_normal((2, 4, 8)).astype(np.float32)
+    out = decode_attention(q, k, v, [30, 12], window=1)
+    for b, t in ((0, 29), (1, 11)):
+        for h in range(4):
+            assert np.array_equal(out[b, h], v[b, t, h // 2].astype(np.float64))
+
+
+def test_window_covering_everything_equals_full_attention(rng):
+    k, v = _contig(rng, 2, 1, 40, 16)
+    q = (rng.standard_normal((2, 2, 16)) * 2).astype(np.float32)
+    full = decode_attention(q, k, v, [40, 25])
+    assert np.array_equal(decode_attention(q, k, v, [40, 25], window=40, num_sinks=3), full)
+    assert np.array_equal(decode_attention(q, k, v, [40, 25], window=1000), full)
+
+
+def test_sinks_plus_window_equal_attention_over_the_kept_rows(rng):
+    """Attention restricted to sinks + window equals full attention over a cache that holds only
+    those rows, assembled by hand."""
+    B, hkv, T, d = 1, 2, 50, 16
+    k, v = _contig(rng, B, hkv, T, d)
+    q = (rng.standard_normal((B, 4, d)) * 2).astype(np.float32)
+    kept = list(range(4)) + list(range(T - 9, T))
+    got = decode_attention(q, k, v, [T], window=9, num_sinks=4)
+    want = decode_attention(q, k[:, kept], v[:, kept], [len(kept)])
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+def test_windowed_numpy_oracle_matches_fsum(rng):
+    B, hkv, T, d = 2, 2, 45, 8
+    k, v = _contig(rng, B, hkv, T, d)
+    q = (rng.standard_normal((B, 4, d)) * 2).astype(np.float32)
+    for window, sinks in ((7, 0), (7, 3), (20, 30)):
+        ref = decode_attention(q, k, v, [45, 33], window=window, num_sinks=sinks)
+        alt = np.array(decode_attention_fsum(q.tolist(), k.tolist(), v.tolist(), [45, 33],
+                                             window=window, num_sinks=sinks))
+        np.testing.assert_allclose(ref, alt, rtol=1e-13, atol=1e-15)

@@ -130,3 +130,38 @@ def test_oracle_sample_renumbers_blocks():
             a = part["k_cache"][part["block_table"][i, j]]
             b = full["k_cache"][full["block_table"][s, j]]
             assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("paged,layout", [(True, "head_major"), (True, "token_major"),
+                                          (False, "head_major"), (False, "token_major")])
+def test_window_poisons_exactly_the_unattended_positions(paged, layout):
+    """With a window, every position outside the first num_sinks and the last W positions holds
+    NaN in K and V; every attended position holds the same finite value as without a window."""
+    from oracle import attended_positions, decode_attention
+    ctx = (200, 37, 96, 5)
+    kw = dict(batch=4, ctx=ctx, paged=paged, layout=layout, num_sinks=3, block_size=16,
+              capacity=None if paged else 210)
+    plain = W.make_workload(W.preset("C5", **kw))
+    win = W.make_workload(W.preset("C5", window=40, **kw))
+    a, b = W.oracle_view(plain), W.oracle_view(win)
+    isnan = lambda u: (u & 0x7FFF) > 0x7F80  # noqa: E731
+    for s, length in enumerate(ctx):
+        keep = set(attended_positions(length, 40, 3).tolist())
+        for t in range(length):
+            if paged:
+                blk, slot = a["block_table"][s, t // 16], t % 16
+            else:
+                blk, slot = s, t
+            for name in ("k_cache", "v_cache"):
+                x, y = a[name][blk, slot], b[name][blk, slot]
+                if t in keep:
+                    assert np.array_equal(x, y) and not isnan(y).any(), (s, t, name)
+                else:
+                    assert isnan(y).all(), (s, t, name)
+    # The oracle never touches the poisoned rows: same result as over the clean cache.
+    bs = a["block_size"] if paged else None
+    ref = decode_attention(a["q"], a["k_cache"], a["v_cache"], a["ctx_lens"], a["block_table"],
+                           block_size=bs, window=40, num_sinks=3)
+    got = decode_attention(b["q"], b["k_cache"], b["v_cache"], b["ctx_lens"], b["block_table"],
+                           block_size=bs, window=40, num_sinks=3)
+    assert np.isfinite(got).all() and np.array_equal(ref, got)
