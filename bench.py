@@ -10,12 +10,17 @@ last-level cache so every step streams from HBM).
 
 Measurement (Ch. 10 "System Model of Throughput and Latency" §8: warm up, time on the device
 with events, never time host submission):
-  * pass A: W warm-up steps (default: >= 0.25 s of GPU work), then K steps bracketed by device
-    events on the launch stream, with
-    torch.cuda.synchronize() on both sides -> ms_per_step, value = unique KV bytes / step time;
-  * pass B: K more steps whose split-kernel launches run back to back between device events ->
-    that kernel's average duration, and roofline.achieved = its unique KV bytes per launch /
+  * pass A: W warm-up steps (default: >= 0.25 s of GPU work), then K steps launched from the
+    host as a serving loop would (``--step-graph`` replays a captured HIP graph of one step
+    instead), bracketed by device events on the launch stream, with torch.cuda.synchronize()
+    on both sides -> ms_per_step, value = unique KV bytes / step time;
+  * pass B: K rounds of split-kernel launches only (at least 8 per round), captured once in a
+    HIP graph and replayed (``--eager`` launches them from the host), back to back between two
+    device events -> that kernel's average duration, free of host-submission gaps even for
+    launches of a few microseconds, and roofline.achieved = its unique KV bytes per launch /
     that duration (the merge launches follow outside the events);
+  * with --window W, only the attended positions (the first sinks and the last W) count as
+    bytes, both in value and in roofline.achieved;
   * cpu_baseline: the fp64 oracle (oracle/) timed on the host on a bounded sample of the same
     workload (whole (layer, sequence, KV head) units in order, about 15 s of CPU work).
 
@@ -80,6 +85,12 @@ def parse_args():
     ap.add_argument("--attn-sinks", type=int, default=None,
                     help="with --window: leading positions always attended (default: the "
                          "workload's sink count)")
+    ap.add_argument("--eager", action="store_true",
+                    help="pass B: launch the split kernels from the host instead of replaying a "
+                         "captured HIP graph")
+    ap.add_argument("--step-graph", action="store_true",
+                    help="pass A: replay each step from a captured HIP graph instead of launching "
+                         "it from the host (a graph launch costs a few microseconds of its own)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run plain device copies of this size (counter calibration runs)")
     return ap.parse_args()
@@ -153,52 +164,72 @@ def main():
             for c in calls:
                 c.decode()
 
+    def capture(fn):
+        """``fn``'s launches captured once in a HIP graph (torch's capture stream is the current
+        stream the library launches on). Replaying it issues them back to back with no host work
+        in between, so small launches are not timed at the host's submission rate."""
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        torch.cuda.synchronize()
+        return graph.replay
+
     # ---- pass A: whole steps -------------------------------------------------------------------
     # The first tens of milliseconds of sustained load on a fresh device run measurably slower
     # (kernel durations drift for ~50-100 launches, then settle), so the default warm-up covers
     # at least 0.25 s of GPU work.
+    run_step = capture(step) if args.step_graph else step
     if args.warmup is None:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        step()
+        run_step()
         torch.cuda.synchronize()
         args.warmup = max(5, int(0.25 / max(time.perf_counter() - t0, 1e-6)) + 1)
     for _ in range(args.warmup):
-        step()
+        run_step()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
-        step()
+        run_step()
     e1.record()
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     print(f"[bench] pass A done: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     # ---- pass B: the split kernel alone, launched back to back ------------------------------------
-    # Events bracket each step's run of split launches (one per layer, same stream, nothing in
-    # between), so the average launch duration carries no per-launch event overhead.
-    # With fewer than 8 layers, each bracket repeats the layer loop so that it holds at least
-    # 8 launches (a lone launch between two events also times the events themselves).
+    # Two events bracket K rounds of split launches (each round: every layer's launch, repeated so
+    # that a round holds at least 8 launches; same stream, nothing in between), so the average
+    # launch duration carries neither event nor host-submission overhead.
     reps = max(1, -(-8 // len(calls)))
-    split_ms = []
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
+
+    def split_round():
         for _ in range(reps):
             for c in calls:
                 c.split()
-        b.record()
-        for c in calls:  # keep the outputs complete (merge pass), outside the bracket
-            c.merge()
-        split_ms.append((a, b))
+
+    run_round = split_round if args.eager else capture(split_round)
     torch.cuda.synchronize()
-    split_ms = [a.elapsed_time(b) / (reps * len(calls)) for a, b in split_ms]
-    split_us_avg = 1e3 * sum(split_ms) / len(split_ms)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        run_round()
+    b.record()
+    for c in calls:  # keep the outputs complete (merge pass), outside the bracket
+        c.merge()
+    torch.cuda.synchronize()
+    launches_timed = args.steps * reps * len(calls)
+    split_us_avg = 1e3 * a.elapsed_time(b) / launches_timed
     print(f"[bench] pass B done: split kernel {split_us_avg:.1f} us/launch", file=sys.stderr, flush=True)
 
     append_info = None
@@ -295,7 +326,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_us": round(split_us_avg, 2),
-            "launches_timed": len(split_ms) * len(calls) * reps,
+            "launches_timed": launches_timed,
+            "timed_by": "host launches" if args.eager else "HIP graph replay",
         },
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "outputs_finite": finite,
