@@ -17,8 +17,11 @@ online_softmax
 fsum_reference
     A second, pure-Python (math.fsum) implementation of the plain definition for tiny shapes.
 kv_append
-    Writing one new token's K/V rows into a contiguous or block-table cache (the step before
+    Writing new tokens' K/V rows into a contiguous or block-table cache (the step before
     attention).
+verify_attention
+    γ new query tokens per sequence attending causally among themselves (the target model's
+    check of a speculative-decoding draft).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed forms, invariants,
 brute force and the independent pure-Python implementation (no function is "parity unpinned").
@@ -43,3 +46,4 @@ from .online_softmax import (  # noqa: F401
 )
 from .fsum_reference import decode_attention_fsum  # noqa: F401
 from .kv_append import append_kv  # noqa: F401
+from .verify_attention import verify_attention  # noqa: F401

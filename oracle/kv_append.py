@@ -22,31 +22,39 @@ __all__ = ["append_kv"]
 
 def append_kv(cache: np.ndarray, new_rows: np.ndarray, positions, block_table=None, *,
               block_size: int | None = None, capacity: int | None = None) -> np.ndarray:
-    """Return a copy of ``cache`` with ``new_rows[b, kv_head, :]`` stored at logical position
-    ``positions[b]`` of sequence ``b`` for every KV head.
+    """Return a copy of ``cache`` with the new rows of every sequence stored.
 
-    ``cache`` is indexed ``[block, slot, kv_head, dim]`` (any storage dtype, copied bit for bit);
-    ``new_rows`` is ``[B, h_kv, dim]`` of the same dtype. Without a block table the cache is
-    contiguous per sequence (block ``b``, slot = position) and ``capacity`` bounds the position;
-    with one, ``block_table.shape[1] * block_size`` does.
+    ``new_rows`` is ``[B, h_kv, dim]`` (one new token per sequence, stored at logical position
+    ``positions[b]``) or ``[B, n, h_kv, dim]`` (n new tokens, token i stored at
+    ``positions[b] + i``, e.g. the γ proposed tokens of a verification step), of the cache's
+    dtype. ``cache`` is indexed ``[block, slot, kv_head, dim]`` (any storage dtype, copied bit
+    for bit). Without a block table the cache is contiguous per sequence (block ``b``, slot =
+    position) and ``capacity`` bounds the position; with one, ``block_table.shape[1] *
+    block_size`` does. A negative first position skips the whole sequence; single tokens at or
+    past the bound are skipped.
     """
     out = np.array(cache, copy=True)
     new_rows = np.asarray(new_rows)
     if new_rows.dtype != out.dtype:
         raise TypeError("new rows and cache must share a storage dtype")
-    for b, pos in enumerate(np.asarray(positions).tolist()):
-        pos = int(pos)
-        if pos < 0:
+    if new_rows.ndim == 3:
+        new_rows = new_rows[:, None]
+    if block_table is None:
+        limit = capacity if capacity is not None else out.shape[1]
+    else:
+        bt = np.asarray(block_table)
+        limit = bt.shape[1] * block_size
+    for b, first in enumerate(np.asarray(positions).tolist()):
+        first = int(first)
+        if first < 0:
             continue
-        if block_table is None:
-            limit = capacity if capacity is not None else out.shape[1]
+        for i in range(new_rows.shape[1]):
+            pos = first + i
             if pos >= limit:
                 continue
-            blk, slot = b, pos
-        else:
-            bt = np.asarray(block_table)
-            if pos >= bt.shape[1] * block_size:
-                continue
-            blk, slot = int(bt[b, pos // block_size]), pos % block_size
-        out[blk, slot] = new_rows[b]
+            if block_table is None:
+                blk, slot = b, pos
+            else:
+                blk, slot = int(bt[b, pos // block_size]), pos % block_size
+            out[blk, slot] = new_rows[b, i]
     return out

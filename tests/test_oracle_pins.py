@@ -380,3 +380,98 @@ def test_windowed_numpy_oracle_matches_fsum(rng):
         alt = np.array(decode_attention_fsum(q.tolist(), k.tolist(), v.tolist(), [45, 33],
                                              window=window, num_sinks=sinks))
         np.testing.assert_allclose(ref, alt, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------------------------
+# γ-query verification attention (Ch. 19 §19.8)
+
+
+def _masked_matrix_attention(q, keys, values, scale, gamma, window=None, sinks=0):
+    """Causal attention written as one masked score matrix (the prefill-style form): S = scale ·
+    Q Kᵀ over all T positions, entries a query may not see set to -inf, row-wise softmax, times
+    V. q: [γ, d]; keys/values: [T, d] fp64."""
+    T = keys.shape[0]
+    s = scale * (q @ keys.T)
+    t = np.arange(T)[None, :]
+    last = (T - gamma + np.arange(gamma))[:, None]       # position of query j
+    visible = t <= last
+    if window is not None:
+        visible &= (t < sinks) | (t > last - window)
+    s = np.where(visible, s, -np.inf)
+    out = np.zeros((gamma, values.shape[1]))
+    for j in range(gamma):
+        if not visible[j].any():
+            continue
+        w = np.exp(s[j] - s[j].max())
+        out[j] = (w @ values) / w.sum()
+    return out
+
+
+def test_one_query_is_plain_decode(rng):
+    from oracle import verify_attention
+    k, v = _contig(rng, 2, 2, 33, 16)
+    q = rng.standard_normal((2, 1, 4, 16)).astype(np.float32)
+    got = verify_attention(q, k, v, [33, 9])
+    assert np.array_equal(got[:, 0], decode_attention(q[:, 0], k, v, [33, 9]))
+
+
+@pytest.mark.parametrize("window,sinks", [(None, 0), (5, 0), (6, 2), (40, 3)])
+def test_verification_equals_the_masked_matrix_form(rng, window, sinks):
+    """Per-query truncated decode (the oracle) against the single masked score matrix, on a
+    paged GQA cache; keys/values for the matrix form are gathered by hand."""
+    from oracle import verify_attention
+    B, gamma, hkv, g, d, bs = 2, 5, 2, 3, 16, 16
+    lens = [37, 6]
+    nblk = 6
+    kc = rng.standard_normal((nblk, bs, hkv, d)).astype(np.float32)
+    vc = rng.standard_normal((nblk, bs, hkv, d)).astype(np.float32)
+    table = np.array([[5, 0, 3], [2, 4, 1]])
+    q = (rng.standard_normal((B, gamma, hkv * g, d)) * 2).astype(np.float32)
+    got = verify_attention(q, kc, vc, lens, table, block_size=bs, window=window, num_sinks=sinks)
+    for b, T in enumerate(lens):
+        for kvh in range(hkv):
+            keys = np.stack([kc[table[b, t // bs], t % bs, kvh] for t in range(T)]).astype(np.float64)
+            vals = np.stack([vc[table[b, t // bs], t % bs, kvh] for t in range(T)]).astype(np.float64)
+            for i in range(g):
+                h = kvh * g + i
+                want = _masked_matrix_attention(q[b, :, h].astype(np.float64), keys, vals,
+                                                1 / math.sqrt(d), gamma, window, sinks)
+                np.testing.assert_allclose(got[b, :, h], want, rtol=1e-13, atol=1e-15)
+
+
+def test_later_positions_do_not_reach_earlier_queries(rng):
+    """Changing the K/V of the last position changes only the last query's output."""
+    from oracle import verify_attention
+    k, v = _contig(rng, 1, 1, 20, 8)
+    q = rng.standard_normal((1, 4, 2, 8)).astype(np.float32)
+    a = verify_attention(q, k, v, [20])
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 19] += 3.0
+    v2[0, 19] -= 2.0
+    b = verify_attention(q, k2, v2, [20])
+    assert np.array_equal(a[0, :3], b[0, :3])
+    assert not np.allclose(a[0, 3], b[0, 3])
+
+
+def test_queries_shorter_than_the_draft_give_zero_rows(rng):
+    from oracle import verify_attention
+    k, v = _contig(rng, 1, 1, 8, 8)
+    q = rng.standard_normal((1, 5, 1, 8)).astype(np.float32)
+    out = verify_attention(q, k, v, [3])                 # T = 3 < γ = 5
+    assert not out[0, :2].any()                          # T_j = -1, 0
+    np.testing.assert_array_equal(out[0, 2, 0], v[0, 0, 0].astype(np.float64))  # T_j = 1
+
+
+def test_append_many_rows_equals_appending_them_one_by_one(rng):
+    from oracle import append_kv
+    B, n, hkv, d, bs = 2, 3, 2, 4, 16
+    cache = rng.standard_normal((5, bs, hkv, d)).astype(np.float32)
+    table = np.array([[3, 1], [0, 4]])
+    new = rng.standard_normal((B, n, hkv, d)).astype(np.float32)
+    pos = [14, 30]                                     # sequence 0 crosses a block edge
+    got = append_kv(cache, new, pos, table, block_size=bs)
+    want = cache
+    for i in range(n):
+        want = append_kv(want, new[:, i], [p + i for p in pos], table, block_size=bs)
+    assert np.array_equal(got, want)
+    assert np.array_equal(got[1, 0], new[0, 2]) and np.array_equal(got[4, 15], new[1, 1])
