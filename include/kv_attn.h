@@ -33,6 +33,15 @@
  * - ctx_lens[b] counts every position in the cache, the current token included (the caller has
  *   already appended it). Without a window every one of them is attended; ctx_lens[b] == 0
  *   gives an output row of zeros.
+ * - Several query tokens (params.num_queries = gamma > 1): Ch. 19 §19.8 checks the gamma tokens
+ *   a draft model proposed in one pass of the target model. Their K/V rows are already in the
+ *   cache as its last gamma positions (ctx_lens[b] = T counts them), q and out are
+ *   [batch, gamma, num_q_heads, head_dim], and query token j (0-based) attends causally to the
+ *   first T - gamma + 1 + j positions (none if that is <= 0: a zero row). Every KV element is
+ *   still read once for all gamma * g query rows of its KV head; scores and P.V then run on the
+ *   matrix cores (P enters the product as the sum of two bf16 parts, about 16 significant
+ *   bits). With a window, each token applies it to its own visible prefix. kv_attn_append_decode
+ *   writes the gamma new rows at positions T - gamma .. T - 1 (nothing when T < gamma).
  * - Sliding window with attention sinks (params.window > 0): a sequence of length T attends
  *   only to its first min(num_sinks, T) positions and its last min(window, T) positions, each
  *   position once. Ch. 19 §19.4.3 bounds the cache of a long sequence by keeping only a recent
@@ -51,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KV_ATTN_ABI_VERSION 2
+#define KV_ATTN_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum kv_attn_status {
@@ -74,8 +83,9 @@ typedef enum kv_attn_dtype {
 /*
  * Problem description.
  *
- * q        : [batch, num_q_heads, head_dim], contiguous, q_dtype.
- * out      : [batch, num_q_heads, head_dim], contiguous, fp32.
+ * q        : [batch, num_queries, num_q_heads, head_dim], contiguous, q_dtype (num_queries = 1:
+ *            [batch, num_q_heads, head_dim]).
+ * out      : the shape of q, contiguous, fp32.
  * k_cache,
  * v_cache  : element (block, token-in-block, kv_head, i) lives at
  *              base + block*stride_block + token*stride_token + kv_head*stride_head + i
@@ -108,7 +118,10 @@ typedef struct kv_attn_params {
   int64_t v_stride_block, v_stride_token, v_stride_head; /* elements, >= 0 */
   int32_t num_sinks;          /* >= 0; leading positions attended as well when window > 0
                                  (ignored when window == 0) */
-  int32_t reserved;           /* must be 0 */
+  int32_t num_queries;        /* query tokens per sequence, gamma (0 means 1); gamma > 1 is the
+                                 verification step of speculative decoding, see below; needs
+                                 bf16 q and KV and gamma * (num_q_heads / num_kv_heads) <= 32,
+                                 gamma <= 16 */
 } kv_attn_params;
 
 /* The launch plan kv_attn_decode will use for a problem (split planning). */
@@ -116,8 +129,10 @@ typedef struct kv_attn_plan {
   int32_t num_splits;       /* S: splits per (sequence, KV head) */
   int32_t split_len;        /* positions per split, a multiple of 16 */
   int32_t grid_split;       /* workgroups of the split kernel: batch * num_kv_heads * S */
-  int32_t grid_merge;       /* workgroups of the merge kernel (0 when S == 1) */
-  int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores */
+  int32_t grid_merge;       /* workgroups of the merge kernel: batch * num_queries *
+                               num_q_heads (0 when S == 1) */
+  int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores,
+                               2: bf16 MFMA scores and P.V for num_queries > 1 */
   int32_t group_padded;     /* compiled group width (power of two >= g) */
   int32_t num_cus;          /* compute units the plan was made for */
   int32_t reserved;
@@ -137,7 +152,8 @@ const char* kv_attn_status_string(int32_t status);
  * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
  * workgroups number at least about one per compute unit, each split spans 16..256 tiles, and a
  * caller-given num_splits overrides the count. With a window the tiles counted are those a
- * sequence can visit: ceil(min(num_sinks, max_ctx_len) / 16) + ceil(window / 16) + 1 at most.
+ * sequence can visit: ceil(min(num_sinks, max_ctx_len) / 16) + ceil((window + gamma - 1) / 16)
+ * + 1 at most, gamma being num_queries (the union of the gamma query tokens' windows).
  * Writes *plan only on KV_ATTN_OK.
  */
 kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_attn_plan* plan);
@@ -155,7 +171,8 @@ size_t kv_attn_workspace_size(const kv_attn_params* p);
  *                       Entries past ceil(ctx_lens[b] / block_size) are never read.
  * ctx_lens            : device int32 [batch]; contract 0 <= ctx_lens[b] <= max_ctx_len (values
  *                       outside are clamped into that range).
- * out                 : device fp32 [batch, num_q_heads, head_dim]; must not alias any input.
+ * out                 : device fp32 [batch, num_q_heads, head_dim] ([batch, gamma, num_q_heads,
+ *                       head_dim] with gamma = num_queries > 1); must not alias any input.
  * workspace           : device scratch of at least kv_attn_workspace_size(p) bytes when the plan
  *                       has more than one split (may be NULL otherwise); contents need no
  *                       initialisation and are left unspecified.
@@ -173,8 +190,9 @@ kv_attn_status kv_attn_decode(const void* q, const void* k_cache, const void* v_
  *
  * kv_attn_decode_split: the streaming pass. With a one-split plan it writes `out` and the merge
  * pass is a no-op. Otherwise it leaves every split's running state in the workspace: the
- * unnormalised sums O at byte offset 0 as fp32 [batch * num_q_heads, S, head_dim] and (m, l) at
- * byte offset plan.ml_offset as fp32 [batch * num_q_heads, S, 2], m being a base-2 maximum (see
+ * unnormalised sums O at byte offset 0 as fp32 [rows, S, head_dim] and (m, l) at byte offset
+ * plan.ml_offset as fp32 [rows, S, 2], rows = batch * gamma * num_q_heads in the row order of
+ * `out` (gamma = 1 for a single query token), m being a base-2 maximum (see
  * kv_attn_merge). Split s of sequence b covers positions [s * split_len, (s+1) * split_len) of
  * that sequence; splits starting at or past ctx_lens[b] are not written. With a window the
  * split covers the same number of 16-position tiles, counted over the visited tiles only (the
@@ -215,9 +233,11 @@ kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
 /*
  * Append one token's K and V rows per sequence to the cache: the step that precedes attention
  * in every decode step (Ch. 10 §4 counts this new-KV write; Ch. 19 §19.7.3 grows a paged cache
- * block by block through the block table).
+ * block by block through the block table). With p->num_queries = n > 1, n consecutive tokens
+ * per sequence (a speculative draft, Ch. 19 §19.8) at positions[b] .. positions[b] + n - 1.
  *
- * k_new, v_new : device, kv_dtype, contiguous [batch, num_kv_heads, head_dim], 16-byte aligned.
+ * k_new, v_new : device, kv_dtype, contiguous [batch, num_kv_heads, head_dim] (n > 1:
+ *                [batch, n, num_kv_heads, head_dim]), 16-byte aligned.
  * k_cache,
  * v_cache      : the caches described by p (strides, block_size, block_table as for decode);
  *                written in place at one slot per (sequence, KV head) and nowhere else.
@@ -235,8 +255,10 @@ kv_attn_status kv_attn_append(const void* k_new, const void* v_new, void* k_cach
 /*
  * kv_attn_append then kv_attn_decode in one call: the new token of sequence b is the last
  * position ctx_lens[b] counts, so it is written at position ctx_lens[b] - 1 (nothing for an empty
- * sequence) and then attended together with the cached ones. Arguments as for the two calls;
- * every check of both runs before anything is launched.
+ * sequence) and then attended together with the cached ones; with gamma = num_queries > 1 the
+ * gamma new tokens are written at ctx_lens[b] - gamma .. ctx_lens[b] - 1 (nothing when
+ * ctx_lens[b] < gamma). Arguments as for the two calls; every check of both runs before
+ * anything is launched.
  */
 kv_attn_status kv_attn_append_decode(const void* q, const void* k_new, const void* v_new,
                                      void* k_cache, void* v_cache, const int32_t* block_table,

@@ -133,8 +133,9 @@ AppendArgs append_args(const kv_attn_params* p, const void* k_new, const void* v
   a.max_blocks = paged ? p->max_blocks_per_seq : 0;
   a.limit = paged ? int32_t(std::min<int64_t>(int64_t(p->max_blocks_per_seq) * p->block_size, 0x7fffffff))
                   : p->block_size;
+  a.rows_per_seq = p->num_queries > 1 ? p->num_queries : 1;
   a.pos_offset = pos_offset;
-  a.total = p->batch * p->num_kv_heads * a.row_chunks;
+  a.total = p->batch * a.rows_per_seq * p->num_kv_heads * a.row_chunks;
   return a;
 }
 
@@ -179,9 +180,10 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
                        : nullptr;
 
   if (passes & kPassAppend) {
-    // The current token is the last position ctx_lens[b] counts: write it before reading.
+    // The current token(s) are the last positions ctx_lens[b] counts: write them before reading.
+    const int32_t nq = p->num_queries > 1 ? p->num_queries : 1;
     const AppendArgs ap = append_args(p, k_new, v_new, const_cast<void*>(k_cache),
-                                      const_cast<void*>(v_cache), block_table, ctx_lens, -1);
+                                      const_cast<void*>(v_cache), block_table, ctx_lens, -nq);
     if (launch_append(ap, stream) != 0) return KV_ATTN_ERR_HIP;
   }
   if (passes & kPassSplit) {
@@ -210,6 +212,7 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.num_splits = plan.num_splits;
     a.window = p->window;
     a.num_sinks = p->num_sinks;
+    a.num_queries = plan.num_queries;
     const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
     a.scale_log2 = float(scale * 1.4426950408889634);  // log2(e)
     if (launch_split(a, plan, p->head_dim, paged, p->q_dtype == KV_ATTN_BF16,
@@ -223,13 +226,14 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     m.num_valid = nullptr;
     m.ctx_lens = ctx_lens;
     m.out = out;
-    m.rows = p->batch * p->num_q_heads;
+    m.rows = p->batch * plan.num_queries * p->num_q_heads;
     m.num_splits = plan.num_splits;
-    m.h_q = p->num_q_heads;
+    m.h_q = plan.num_queries * p->num_q_heads;
     m.split_tiles = plan.split_tiles;
     m.max_ctx = p->max_ctx_len;
     m.window = p->window;
     m.num_sinks = p->num_sinks;
+    m.num_queries = plan.num_queries;
     if (launch_merge(m, p->head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
   }
   if (debug_mode()) {
@@ -318,6 +322,7 @@ kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
   m.max_ctx = 0;
   m.window = 0;
   m.num_sinks = 0;
+  m.num_queries = 1;
   if (kvattn::launch_merge(m, head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
   if (kvattn::debug_mode()) {
     if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess ||

@@ -23,6 +23,8 @@ constexpr int kMinSplitTiles = 16;     // a split spans at least 256 positions .
 constexpr int kMaxSplitTiles = 256;    // ... and at most 4096 positions
 constexpr int kWorkgroupsPerCu = 1;    // target split workgroups per compute unit
 constexpr int kMaxSplits = 4096;
+constexpr int kMaxQueryRows = 32;      // rows mode: num_queries * group <= 32 (two MFMA blocks)
+constexpr int kMaxQueries = 16;
 
 // Everything the split kernel needs, by value.
 struct SplitArgs {
@@ -47,6 +49,7 @@ struct SplitArgs {
   float scale_log2;            // scale * log2(e)
   int32_t window;              // > 0: attend only the last `window` positions plus the sinks
   int32_t num_sinks;           // leading positions always attended when a window is set
+  int32_t num_queries;         // query tokens per sequence (rows mode; 1 otherwise)
 };
 
 struct MergeArgs {
@@ -57,17 +60,18 @@ struct MergeArgs {
   float* out;                  // [rows, d]
   int32_t rows;
   int32_t num_splits;
-  int32_t h_q;                 // decode path: row / h_q is the sequence
+  int32_t h_q;                 // decode path: rows per sequence (row / h_q is the sequence)
   int32_t split_tiles;         // decode path: tiles per split
   int32_t max_ctx;             // decode path: clamp of ctx_lens
   int32_t window;              // decode path: as in SplitArgs
   int32_t num_sinks;
+  int32_t num_queries;
 };
 
 // Everything the append kernel needs: one new K/V row per (sequence, KV head) is stored at
 // logical position positions[b] + pos_offset of sequence b.
 struct AppendArgs {
-  const void* k_new;           // [B, h_kv, d] contiguous
+  const void* k_new;           // [B, rows_per_seq, h_kv, d] contiguous
   const void* v_new;
   void* k;                     // caches (same layout rules as the split kernel)
   void* v;
@@ -81,15 +85,18 @@ struct AppendArgs {
   int32_t bs_log2;             // paged only
   int32_t max_blocks;          // paged only
   int32_t limit;               // positions at or past it are not written
-  int32_t pos_offset;          // 0, or -1 when positions are context lengths
-  int32_t total;               // B * h_kv * row_chunks
+  int32_t pos_offset;          // 0, or -rows_per_seq when positions are context lengths
+  int32_t rows_per_seq;        // new tokens per sequence, stored at positions[b] + pos_offset + i
+  int32_t total;               // B * rows_per_seq * h_kv * row_chunks
 };
 
 struct Plan {
   int32_t num_splits;
   int32_t split_tiles;
   int32_t group_padded;
-  int32_t variant;  // 0: vector fp32 path, 1: MFMA scores
+  int32_t variant;  // 0: vector fp32 path, 1: MFMA scores, 2: MFMA scores and P.V (rows mode)
+  int32_t num_queries;  // query tokens per sequence (>= 1)
+  int32_t row_blocks;   // rows mode: blocks of 16 query rows per (sequence, KV head)
   int64_t grid_split;
   int64_t grid_merge;
   uint64_t workspace_bytes;

@@ -43,6 +43,7 @@ namespace kvattn {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -173,7 +174,10 @@ __device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
 #endif
 
 // PAGED: 0 contiguous, 1 paged, 2 decided at run time (vector variant only).
-template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED>
+// R = 0: one query token per sequence (G = compiled group width). R > 0 ("rows" mode, variant 2):
+// num_queries tokens per sequence, the group's query rows (token-major, then head) packed into R
+// blocks of 16 MFMA columns; scores and P.V both on the matrix cores (G unused).
+template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED, int R = 0>
 __global__ __launch_bounds__(kSplitThreads)
 #if KV_ATTN_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(MFMA && G <= 8 ? KV_ATTN_WAVES_PER_EU : 1)))
@@ -181,6 +185,9 @@ __attribute__((amdgpu_waves_per_eu(MFMA && G <= 8 ? KV_ATTN_WAVES_PER_EU : 1)))
 void split_kernel(const SplitArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(!MFMA || (Q_BF16 && KV_BF16), "matrix-core scores need bf16 q and KV");
+  static_assert(R == 0 || MFMA, "rows mode runs on the matrix cores");
+  constexpr bool ROWS = R > 0;
+  constexpr int NR = ROWS ? 16 * R : G;       // query rows held per (sequence, KV head)
   constexpr int EPL = D / 16;                 // elements per lane of a 16-lane row
   constexpr int KVB = KV_BF16 ? 2 : 4;        // bytes per KV element
   constexpr int QB = Q_BF16 ? 2 : 4;
@@ -208,25 +215,34 @@ void split_kernel(const SplitArgs a) {
 
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  const int nq = ROWS ? a.num_queries : 1;  // query tokens per sequence (the last nq positions)
   // Attended positions: all of [0, ctx), or with a window W the sinks [0, sink_end) and the
-  // recent positions [win_start, ctx). Their tiles are enumerated as "virtual" tiles: the
-  // n_first tiles of the sink range, then the tiles from win_tile0 to the last tile (a tile is
-  // never visited twice when the two ranges meet). Without a window sink_end = win_start = 0.
+  // recent positions [win_start, ctx) (with nq query tokens, the union of their windows). Their
+  // tiles are enumerated as "visited" tiles: the n_first tiles of the sink range, then the tiles
+  // from win_tile0 to the last tile (a tile is never visited twice when the two ranges meet).
+  // Without a window sink_end = win_start = 0.
   int sink_end = 0, win_start = 0, n_first = 0, win_tile0 = 0;
   if (a.window > 0) {
     sink_end = min(a.num_sinks, ctx);
-    win_start = max(ctx - a.window, 0);
+    win_start = max(ctx - (nq - 1) - a.window, 0);
     n_first = (sink_end + kTile - 1) / kTile;
     win_tile0 = max(win_start / kTile, n_first);
   }
   const int ntiles = n_first + max((ctx + kTile - 1) / kTile - win_tile0, 0);
   const int t_begin = split * a.split_tiles;
-  const int64_t q_row0 = int64_t(b) * a.h_q + int64_t(kvh) * g;  // first query head of the group
+  const int rows = nq * g;  // query rows of this (sequence, KV head): token-major, then head
+  // Global row of query row rho: token rho / g of sequence b, head kvh * g + rho % g.
+  auto out_row = [&](int rho) __attribute__((always_inline)) {
+    if constexpr (ROWS)
+      return (int64_t(b) * nq + rho / g) * a.h_q + int64_t(kvh) * g + rho % g;
+    else
+      return int64_t(b) * a.h_q + int64_t(kvh) * g + rho;
+  };
   if (t_begin >= ntiles) {
     // Only an empty sequence reaches here with one split: its rows are defined as zeros.
     if (S == 1) {
-      for (int idx = threadIdx.x; idx < g * D; idx += kSplitThreads)
-        a.out[(q_row0 + idx / D) * D + idx % D] = 0.f;
+      for (int idx = threadIdx.x; idx < rows * D; idx += kSplitThreads)
+        a.out[out_row(idx / D) * D + idx % D] = 0.f;
     }
     return;
   }
@@ -235,23 +251,28 @@ void split_kernel(const SplitArgs a) {
   const int n_w = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
 
   // ---- query rows, loaded once ------------------------------------------------------------
-  bf16x8_t qb[KC];      // MFMA B operand: head r16, elements c*32 + q4*8 .. +8
+  constexpr int RB = ROWS ? R : 1;
+  bf16x8_t qb[RB][KC];  // MFMA B operand of block cb: query row 16*cb + r16, elements c*32 + q4*8 .. +8
   float qf[G][EPL];     // vector path: every head, elements r16*EPL .. +EPL
   if constexpr (MFMA) {
     const char* qbase = reinterpret_cast<const char*>(a.q);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (r16 < g)
-        x = *reinterpret_cast<const u32x4_t*>(qbase + ((q_row0 + r16) * D + c * 32 + q4 * 8) * 2);
-      qb[c] = __builtin_bit_cast(bf16x8_t, x);
+    for (int cb = 0; cb < RB; ++cb) {
+      const int rho = 16 * cb + r16;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (rho < rows)
+          x = *reinterpret_cast<const u32x4_t*>(qbase + (out_row(rho) * D + c * 32 + q4 * 8) * 2);
+        qb[cb][c] = __builtin_bit_cast(bf16x8_t, x);
+      }
     }
   } else {
     const char* qbase = reinterpret_cast<const char*>(a.q);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       if (j < g) {
-        const Seg<EPL * QB> s = load_seg<EPL * QB>(qbase + ((q_row0 + j) * D + r16 * EPL) * QB);
+        const Seg<EPL * QB> s = load_seg<EPL * QB>(qbase + (out_row(j) * D + r16 * EPL) * QB);
         widen<EPL, Q_BF16>(s, qf[j]);
       } else {
 #pragma unroll
@@ -272,6 +293,24 @@ void split_kernel(const SplitArgs a) {
     l_v[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) O[j][e] = 0.f;
+  }
+  // Rows mode: per block cb, this lane's query row rho = 16*cb + r16 keeps (m, l) and the
+  // transposed output block O^T[d][rho] of 4*EPL elements (d = EPL*(4*q4 + r) + dc, held in
+  // oT[cb][dc][r]). Token j = rho / g sees positions below lim = ctx - nq + 1 + j; with a window,
+  // those below the sinks or at or past lim - W. Padding rows see nothing.
+  float m_r[RB], l_r[RB];
+  f32x4_t oT[RB][EPL];
+  int lim[RB], wst[RB];
+  const int snk = a.window > 0 ? a.num_sinks : 0;
+#pragma unroll
+  for (int cb = 0; cb < RB; ++cb) {
+    m_r[cb] = neg_inf();
+    l_r[cb] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < EPL; ++dc) oT[cb][dc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int rho = 16 * cb + r16;
+    lim[cb] = rho < rows ? ctx - nq + 1 + rho / g : -1;
+    wst[cb] = a.window > 0 ? lim[cb] - a.window : -1;
   }
 
   // ---- tile addressing -------------------------------------------------------------------------
@@ -376,7 +415,7 @@ void split_kernel(const SplitArgs a) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.kc[c]), qb[c],
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.kc[c]), qb[0][c],
                                                       acc, 0, 0, 0);
       // acc[r] = score of tile row 4*q4 + r for head r16.
       float s[4];
@@ -453,6 +492,84 @@ void split_kernel(const SplitArgs a) {
     }
   };
 
+  // Rows mode: scores S^T[key][row] = K Q^T and O^T[d][row] += V^T P^T, both on the matrix cores.
+  // The score MFMA leaves, in lane (q4, r16), the scores of keys 4*q4 .. 4*q4+3 for query row
+  // r16 of the block, which is exactly the lane layout of the B operand P^T of a 16x16x16 MFMA.
+  // For the A operand V^T the d index of output row m of block dc is taken as EPL*m + dc, so
+  // that lane (q4, r16) needs V[4*q4 + i][EPL*r16 + dc], i = 0..3: elements this lane already
+  // loaded (value rows 4*q4+i, elements EPL*r16 ..), repacked with no data exchange between
+  // lanes. The bf16 operand cannot hold P to fp32 accuracy (a lone probability near 1 would
+  // carry up to 2^-8 relative error into the output), so P is split into p_hi = bf16(p) and
+  // p_lo = bf16(p - p_hi) and both halves are multiplied in: the product then matches fp32 P to
+  // 2^-16 relative, and l keeps the fp32 probabilities.
+  auto compute_rows = [&](int k, const Frag& f) __attribute__((always_inline)) {
+    const int p0 = logical_tile(first + kWaves * k) * kTile;
+    bf16x4_t vt[EPL];
+#pragma unroll
+    for (int dc = 0; dc < EPL; ++dc) {
+      const int w = dc >> 1;
+      uint32_t lo, hi;
+      if (dc & 1) {
+        lo = (f.vr[0].w[w] >> 16) | (f.vr[1].w[w] & 0xffff0000u);
+        hi = (f.vr[2].w[w] >> 16) | (f.vr[3].w[w] & 0xffff0000u);
+      } else {
+        lo = (f.vr[0].w[w] & 0xffffu) | (f.vr[1].w[w] << 16);
+        hi = (f.vr[2].w[w] & 0xffffu) | (f.vr[3].w[w] << 16);
+      }
+      vt[dc] = __builtin_bit_cast(bf16x4_t, u32x2_t{lo, hi});
+    }
+#pragma unroll
+    for (int cb = 0; cb < RB; ++cb) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.kc[c]),
+                                                      qb[cb][c], acc, 0, 0, 0);
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = p0 + 4 * q4 + r;
+        const bool valid = pos < lim[cb] && (pos < snk || pos >= wst[cb]);
+        sc[r] = valid ? acc[r] * a.scale_log2 : neg_inf();
+      }
+      float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mt = max_xor32(max_xor16(mt));
+      const float m_new = fmaxf(m_r[cb], mt);
+      // A row that has seen nothing yet keeps m = -inf; exponentials then use 0 in its place,
+      // so they are 0 instead of NaN.
+      const float m_use = m_new == neg_inf() ? 0.f : m_new;
+      const float c = exp2_fast(m_r[cb] - m_use);
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(sc[r] - m_use);
+      l_r[cb] = c * l_r[cb] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m_r[cb] = m_new;
+      if (__any(16 * cb + r16 < rows && c != 1.0f)) {
+#pragma unroll
+        for (int dc = 0; dc < EPL; ++dc) oT[cb][dc] *= c;
+      }
+      const f32x4_t pf = {pr[0], pr[1], pr[2], pr[3]};
+      const bf16x4_t p_hi = __builtin_convertvector(pf, bf16x4_t);
+      const f32x4_t hi_f = __builtin_convertvector(p_hi, f32x4_t);
+      const bf16x4_t p_lo = __builtin_convertvector(
+          f32x4_t{pf[0] - hi_f[0], pf[1] - hi_f[1], pf[2] - hi_f[2], pf[3] - hi_f[3]}, bf16x4_t);
+      // The two chains are issued one after the other so that consecutive MFMAs write different
+      // accumulators.
+#pragma unroll
+      for (int dc = 0; dc < EPL; ++dc)
+        oT[cb][dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[dc], p_hi, oT[cb][dc], 0, 0, 0);
+#pragma unroll
+      for (int dc = 0; dc < EPL; ++dc)
+        oT[cb][dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[dc], p_lo, oT[cb][dc], 0, 0, 0);
+    }
+  };
+  auto compute = [&](int k, const Frag& f) __attribute__((always_inline)) {
+    if constexpr (ROWS)
+      compute_rows(k, f);
+    else
+      compute_tile(k, f);
+  };
+
   // ---- streaming loop: kDepth tiles in flight --------------------------------------------------
   // The steady-state loop issues its loads unconditionally, so the compiler's wait counts let
   // the kDepth tiles behind the one being computed stay in flight; the last tiles are drained
@@ -464,7 +581,7 @@ void split_kernel(const SplitArgs a) {
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) { load_tile(P(), buf[P()]); });
     do {
       static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
-        compute_tile(k0 + P(), buf[P()]);
+        compute(k0 + P(), buf[P()]);
         load_tile(k0 + P() + kDepth, buf[P()]);
       });
       k0 += kDepth;
@@ -472,12 +589,12 @@ void split_kernel(const SplitArgs a) {
     // Tiles k0 .. k0+kDepth-1 are in flight; at most kDepth-1 more remain after them.
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
       const int k = k0 + P();
-      compute_tile(k, buf[P()]);
+      compute(k, buf[P()]);
       if (k + kDepth < n_w) load_tile(k + kDepth, buf[P()]);
     });
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
       const int k = k0 + kDepth + P();
-      if (k < n_w) compute_tile(k, buf[P()]);
+      if (k < n_w) compute(k, buf[P()]);
     });
   } else {
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
@@ -485,20 +602,35 @@ void split_kernel(const SplitArgs a) {
     });
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
       if (P() < n_w) {
-        compute_tile(P(), buf[P()]);
+        compute(P(), buf[P()]);
         if (P() + kDepth < n_w) load_tile(P() + kDepth, buf[P()]);
       }
     });
     static_for<0, kDepth>([&](auto P) __attribute__((always_inline)) {
-      if (kDepth + P() < n_w) compute_tile(kDepth + P(), buf[P()]);
+      if (kDepth + P() < n_w) compute(kDepth + P(), buf[P()]);
     });
   }
 
   // ---- merge the four wave states through LDS ---------------------------------------------------
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  __shared__ float sm_o[kWaves][G][D];
-  if constexpr (MFMA) {
+  constexpr int DP = ROWS ? D + 4 : D;  // rows mode: padded rows spread its stores over the banks
+  __shared__ float sm_m[kWaves][NR];
+  __shared__ float sm_l[kWaves][NR];
+  __shared__ float sm_o[kWaves][NR][DP];
+  if constexpr (ROWS) {
+#pragma unroll
+    for (int cb = 0; cb < RB; ++cb) {
+      const float lt = sum_xor32(sum_xor16(l_r[cb]));
+      const int rho = 16 * cb + r16;
+      if (q4 == 0) {
+        sm_m[wave][rho] = m_r[cb];
+        sm_l[wave][rho] = lt;
+      }
+#pragma unroll
+      for (int dc = 0; dc < EPL; ++dc)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm_o[wave][rho][EPL * (4 * q4 + r) + dc] = oT[cb][dc][r];
+    }
+  } else if constexpr (MFMA) {
     const float lt = sum_xor32(sum_xor16(l_run));
     if (q4 == 0 && r16 < G) {
       sm_m[wave][r16] = m_run;
@@ -514,23 +646,24 @@ void split_kernel(const SplitArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) O[j][e] = sum_xor32(sum_xor16(O[j][e]));
-  }
-  if (q4 == 0) {
+  if constexpr (!ROWS) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][j][r16 * EPL + e] = O[j][e];
+      for (int e = 0; e < EPL; ++e) O[j][e] = sum_xor32(sum_xor16(O[j][e]));
+    }
+    if (q4 == 0) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm_o[wave][j][r16 * EPL + e] = O[j][e];
+      }
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kSplitThreads) {
+  for (int idx = threadIdx.x; idx < rows * D; idx += kSplitThreads) {
     const int j = idx / D;
     const int e = idx % D;
-    if (j >= g) continue;
     float M = neg_inf();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
@@ -542,9 +675,9 @@ void split_kernel(const SplitArgs a) {
       L = fmaf(ww, sm_l[w][j], L);
       acc = fmaf(ww, sm_o[w][j][e], acc);
     }
-    const int64_t row = q_row0 + j;
+    const int64_t row = out_row(j);
     if (S == 1) {
-      a.out[row * D + e] = acc / L;
+      a.out[row * D + e] = L > 0.f ? acc / L : 0.f;  // L = 0: a query token that sees nothing
     } else {
       const int64_t slot = row * S + split;
       a.o_part[slot * D + e] = acc;
@@ -596,7 +729,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
     int n_first = 0, win_tile0 = 0;
     if (a.window > 0) {
       n_first = (min(a.num_sinks, ctx) + kTile - 1) / kTile;
-      win_tile0 = max(max(ctx - a.window, 0) / kTile, n_first);
+      win_tile0 = max(max(ctx - (a.num_queries - 1) - a.window, 0) / kTile, n_first);
     }
     const int ntiles = n_first + max((ctx + kTile - 1) / kTile - win_tile0, 0);
     nv = (ntiles + a.split_tiles - 1) / a.split_tiles;
@@ -661,10 +794,14 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   const int idx = int(blockIdx.x) * 256 + int(threadIdx.x);
   if (idx >= a.total) return;
   const int chunk = idx % a.row_chunks;
-  const int row = idx / a.row_chunks;  // b * h_kv + kvh
+  const int row = idx / a.row_chunks;  // (b * rows_per_seq + i) * h_kv + kvh
   const int kvh = row % a.h_kv;
-  const int b = row / a.h_kv;
-  const int pos = a.positions[b] + a.pos_offset;
+  const int token = row / a.h_kv;
+  const int b = token / a.rows_per_seq;
+  const int i = token - b * a.rows_per_seq;
+  const int first = a.positions[b] + a.pos_offset;  // < 0: this sequence appends nothing
+  if (first < 0) return;
+  const int pos = first + i;
   if (pos < 0 || pos >= a.limit) return;
   int64_t blk, slot;
   if (a.block_table != nullptr) {
@@ -683,11 +820,23 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(a.v) + vdst) = vx;
 }
 
-template <int D, int G, bool QB, bool KB, bool MF, int PG>
+template <int D, int G, bool QB, bool KB, bool MF, int PG, int R = 0>
 int launch_one(const SplitArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG>), dim3(uint32_t(grid)), dim3(kSplitThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG, R>), dim3(uint32_t(grid)),
+                     dim3(kSplitThreads), 0, stream, a);
   return int(hipGetLastError());
+}
+
+// Rows mode (several query tokens per sequence): bf16 only, 1 or 2 blocks of 16 query rows.
+template <int D>
+int launch_rows(const SplitArgs& a, const Plan& plan, bool paged, hipStream_t s) {
+  switch (plan.row_blocks) {
+    case 1: return paged ? launch_one<D, 1, true, true, true, 1, 1>(a, plan.grid_split, s)
+                         : launch_one<D, 1, true, true, true, 0, 1>(a, plan.grid_split, s);
+    case 2: return paged ? launch_one<D, 1, true, true, true, 1, 2>(a, plan.grid_split, s)
+                         : launch_one<D, 1, true, true, true, 0, 2>(a, plan.grid_split, s);
+    default: return int(hipErrorInvalidValue);
+  }
 }
 
 template <int D, int G>
@@ -721,6 +870,11 @@ int launch_group(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16, 
 int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, bool q_bf16,
                  bool kv_bf16, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (plan.variant == 2) {
+    if (head_dim == 64) return launch_rows<64>(a, plan, paged, s);
+    if (head_dim == 128) return launch_rows<128>(a, plan, paged, s);
+    return int(hipErrorInvalidValue);
+  }
   if (head_dim == 64) return launch_group<64>(a, plan, paged, q_bf16, kv_bf16, s);
   if (head_dim == 128) return launch_group<128>(a, plan, paged, q_bf16, kv_bf16, s);
   return int(hipErrorInvalidValue);

@@ -39,9 +39,9 @@ kv_attn_status validate_params(const kv_attn_params* p) {
   if ((p->q_dtype != KV_ATTN_F32 && p->q_dtype != KV_ATTN_BF16) ||
       (p->kv_dtype != KV_ATTN_F32 && p->kv_dtype != KV_ATTN_BF16))
     return KV_ATTN_ERR_UNSUPPORTED;
-  if (p->reserved != 0) return KV_ATTN_ERR_VALUE;
   if (p->max_ctx_len < 0 || p->num_splits < 0) return KV_ATTN_ERR_VALUE;
-  if (p->window < 0 || p->num_sinks < 0) return KV_ATTN_ERR_VALUE;
+  if (p->window < 0 || p->num_sinks < 0 || p->num_queries < 0) return KV_ATTN_ERR_VALUE;
+  if (p->num_queries > kMaxQueries) return KV_ATTN_ERR_UNSUPPORTED;
   if (!isfinite(p->scale)) return KV_ATTN_ERR_VALUE;
   if (p->block_size < 1 || p->num_blocks < 1) return KV_ATTN_ERR_SHAPE;
   const int64_t strides[6] = {p->k_stride_block, p->k_stride_token, p->k_stride_head,
@@ -75,14 +75,18 @@ kv_attn_status validate_layout(const kv_attn_params* p, bool paged) {
   return KV_ATTN_OK;
 }
 
+int32_t num_queries(const kv_attn_params* p) { return p->num_queries > 1 ? p->num_queries : 1; }
+
 // Tiles of kTile positions a sequence of at most max_ctx_len positions can visit. With a
-// window W and n sinks that is at most ceil(min(n, T)/16) sink tiles plus the ceil(W/16) + 1
-// tiles that W consecutive positions can touch, and never more than the whole sequence's tiles.
+// window W and n sinks that is at most ceil(min(n, T)/16) sink tiles plus the tiles that the
+// W + gamma - 1 consecutive positions of the gamma query tokens' windows can touch, and never
+// more than the whole sequence's tiles.
 int64_t max_visited_tiles(const kv_attn_params* p) {
   const int64_t all = ceil_div(p->max_ctx_len > 0 ? p->max_ctx_len : 1, kTile);
   if (p->window <= 0) return all;
   const int64_t sinks = p->num_sinks < p->max_ctx_len ? p->num_sinks : p->max_ctx_len;
-  const int64_t bounded = ceil_div(sinks, kTile) + ceil_div(p->window, kTile) + 1;
+  const int64_t span = int64_t(p->window) + num_queries(p) - 1;
+  const int64_t bounded = ceil_div(sinks, kTile) + ceil_div(span, kTile) + 1;
   return bounded < all ? bounded : all;
 }
 
@@ -94,6 +98,13 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   const kv_attn_status st = validate_params(p);
   if (st != KV_ATTN_OK) return st;
   if (num_cus < 1) return KV_ATTN_ERR_VALUE;
+  // Several query tokens: the rows-mode kernel takes bf16 q and KV and up to kMaxQueryRows
+  // query rows per KV head.
+  if (p->num_queries > 1) {
+    if (p->q_dtype != KV_ATTN_BF16 || p->kv_dtype != KV_ATTN_BF16) return KV_ATTN_ERR_UNSUPPORTED;
+    if (p->num_queries * (p->num_q_heads / p->num_kv_heads) > kMaxQueryRows)
+      return KV_ATTN_ERR_UNSUPPORTED;
+  }
   const int64_t tiles_max = max_visited_tiles(p);
   const int64_t units = int64_t(p->batch) * p->num_kv_heads;
   int64_t S;
@@ -117,9 +128,17 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   plan->group_padded = padded_group(p->num_q_heads / p->num_kv_heads);
   const bool force_vector = getenv("KV_ATTN_FORCE_VECTOR") != nullptr &&
                             strcmp(getenv("KV_ATTN_FORCE_VECTOR"), "1") == 0;
-  plan->variant = (p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector) ? 1 : 0;
+  const int32_t nq = num_queries(p);
+  plan->num_queries = nq;
+  plan->row_blocks = 0;
+  if (nq > 1) {
+    plan->variant = 2;
+    plan->row_blocks = int32_t(ceil_div(int64_t(nq) * (p->num_q_heads / p->num_kv_heads), 16));
+  } else {
+    plan->variant = (p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector) ? 1 : 0;
+  }
   plan->grid_split = units * S;
-  const int64_t rows = int64_t(p->batch) * p->num_q_heads;
+  const int64_t rows = int64_t(p->batch) * nq * p->num_q_heads;
   plan->grid_merge = S > 1 ? rows : 0;
   if (S > 1) {
     const uint64_t o_bytes = uint64_t(rows) * uint64_t(S) * uint64_t(p->head_dim) * 4u;

@@ -98,7 +98,7 @@ class kv_attn_params(ctypes.Structure):
         ("v_stride_token", ctypes.c_int64),
         ("v_stride_head", ctypes.c_int64),
         ("num_sinks", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("num_queries", ctypes.c_int32),
     ]
 
 
@@ -174,20 +174,22 @@ def make_params(*, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: in
                 max_blocks_per_seq: int = 1, num_splits: int = 0,
                 q_dtype: int = KV_ATTN_BF16, kv_dtype: int = KV_ATTN_BF16,
                 scale: float = 0.0, window: Optional[int] = None,
-                num_sinks: int = 0) -> kv_attn_params:
+                num_sinks: int = 0, num_queries: int = 1) -> kv_attn_params:
     """Fill a ``kv_attn_params`` (strides are (block, token, head) in elements).
 
     ``window=None`` attends every position; an integer W >= 1 attends the last W positions of
-    each sequence plus its first ``num_sinks`` positions.
+    each sequence plus its first ``num_sinks`` positions. ``num_queries`` (gamma) query tokens
+    per sequence attend causally among themselves (the last gamma cached positions).
     """
     if window is not None and int(window) < 1:
         raise ValueError("window must be None (no window) or >= 1")
     p = kv_attn_params()
     p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim = batch, num_q_heads, num_kv_heads, head_dim
     p.block_size, p.max_blocks_per_seq, p.max_ctx_len = block_size, max_blocks_per_seq, max_ctx_len
-    p.num_splits, p.q_dtype, p.kv_dtype, p.scale, p.reserved = num_splits, q_dtype, kv_dtype, scale, 0
+    p.num_splits, p.q_dtype, p.kv_dtype, p.scale = num_splits, q_dtype, kv_dtype, scale
     p.window = 0 if window is None else int(window)
     p.num_sinks = int(num_sinks)
+    p.num_queries = int(num_queries)
     p.num_blocks = num_blocks
     p.k_stride_block, p.k_stride_token, p.k_stride_head = (int(s) for s in k_strides)
     p.v_stride_block, p.v_stride_token, p.v_stride_head = (int(s) for s in v_strides)
@@ -229,7 +231,9 @@ def _check_extent(t: torch.Tensor, strides, blocks: int, slots: int, heads: int,
 class DecodeCall:
     """Checked, marshalled arguments of one decode problem (reusable across launches).
 
-    q: [B, h_q, d] contiguous bf16/fp32; out: [B, h_q, d] contiguous fp32. k_cache/v_cache:
+    q: [B, h_q, d] (one query token per sequence) or [B, gamma, h_q, d] (gamma tokens, the last
+    gamma cached positions, causal among themselves), contiguous bf16/fp32; out: fp32 shaped
+    like q. k_cache/v_cache:
     device tensors of one dtype holding num_kv_heads heads, whose element (block, token, head, i)
     is at block*strides[0] + token*strides[1] + head*strides[2] + i. block_table: int32
     [B, max_blocks] (paged; block_size tokens per block) or None (contiguous; block_size = slot
@@ -243,9 +247,11 @@ class DecodeCall:
                  num_blocks: int, max_ctx_len: Optional[int] = None, scale: float = 0.0,
                  num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
                  window: Optional[int] = None, num_sinks: int = 0):
-        if q.dim() != 3 or not q.is_contiguous():
-            raise ValueError("q must be a contiguous [B, h_q, d] tensor")
-        B, hq, d = q.shape
+        if q.dim() not in (3, 4) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, h_q, d] or [B, gamma, h_q, d] tensor")
+        B, hq, d = q.shape[0], q.shape[-2], q.shape[-1]
+        nq = int(q.shape[1]) if q.dim() == 4 else 1
+        self.num_queries = nq
         if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous fp32 tensor shaped like q")
         if k_cache.dtype != v_cache.dtype:
@@ -273,7 +279,7 @@ class DecodeCall:
             max_ctx_len=int(max_ctx_len), num_blocks=num_blocks, k_strides=k_strides,
             v_strides=v_strides, max_blocks_per_seq=max_blocks, num_splits=num_splits,
             q_dtype=_dtype_code(q.dtype), kv_dtype=_dtype_code(k_cache.dtype), scale=float(scale),
-            window=window, num_sinks=num_sinks)
+            window=window, num_sinks=num_sinks, num_queries=nq)
         _check_extent(k_cache, k_strides, num_blocks, block_size, hkv, d, "k_cache")
         _check_extent(v_cache, v_strides, num_blocks, block_size, hkv, d, "v_cache")
         ws_bytes = kv_attn_workspace_size(self.params)
@@ -311,9 +317,11 @@ class DecodeCall:
             raise KvAttnError(st, "kv_attn_decode_merge")
 
     def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
-        """Write each sequence's new K/V row at position ctx_lens[b] - 1, then decode."""
+        """Write each sequence's new K/V rows at positions ctx_lens[b] - gamma .. ctx_lens[b] - 1
+        (k_new/v_new [B, h_kv, d] for gamma = 1, else [B, gamma, h_kv, d]), then decode."""
         q, k_cache = self._keep[0], self._keep[1]
-        _check_new_rows(k_new, v_new, k_cache, q.shape[0], self.params.num_kv_heads, q.shape[2])
+        _check_new_rows(k_new, v_new, k_cache, q.shape[0], self.params.num_kv_heads, q.shape[-1],
+                        self.num_queries)
         st = _lib.kv_attn_append_decode(self._ptrs[0], k_new.data_ptr(), v_new.data_ptr(),
                                         *self._ptrs[1:], ctypes.byref(self.params), *self._ws,
                                         _stream_handle(stream))
@@ -321,11 +329,12 @@ class DecodeCall:
             raise KvAttnError(st, "kv_attn_append_decode")
 
 
-def _check_new_rows(k_new, v_new, cache, batch, num_kv_heads, head_dim):
+def _check_new_rows(k_new, v_new, cache, batch, num_kv_heads, head_dim, rows=1):
+    want = (batch, num_kv_heads, head_dim) if rows == 1 else (batch, rows, num_kv_heads, head_dim)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
-        if (t.shape != (batch, num_kv_heads, head_dim) or not t.is_contiguous()
+        if (tuple(t.shape) != want or not t.is_contiguous()
                 or t.dtype != cache.dtype or t.device != cache.device):
-            raise ValueError(f"{name} must be a contiguous [B, h_kv, d] tensor of the cache's "
+            raise ValueError(f"{name} must be a contiguous {list(want)} tensor of the cache's "
                              "dtype on its device")
 
 
@@ -350,10 +359,12 @@ def kv_attn_decode_merge(call: DecodeCall, stream=None) -> None:
 def kv_attn_append(k_new, v_new, k_cache, v_cache, block_table, positions, *, num_kv_heads: int,
                    k_strides: Sequence[int], v_strides: Sequence[int], block_size: int,
                    num_blocks: int, stream=None) -> None:
-    """Store k_new/v_new ([B, h_kv, d]) at logical position positions[b] of every sequence."""
+    """Store k_new/v_new ([B, h_kv, d]) at logical position positions[b] of every sequence, or
+    ([B, n, h_kv, d]) n tokens at positions[b] .. positions[b] + n - 1."""
     B = int(positions.shape[0])
     d = int(k_new.shape[-1])
-    _check_new_rows(k_new, v_new, k_cache, B, num_kv_heads, d)
+    n = int(k_new.shape[1]) if k_new.dim() == 4 else 1
+    _check_new_rows(k_new, v_new, k_cache, B, num_kv_heads, d, n)
     if positions.dtype != torch.int32 or not positions.is_contiguous() or positions.device != k_cache.device:
         raise ValueError("positions must be a contiguous int32 [B] tensor on the cache's device")
     if block_table is not None:
@@ -366,7 +377,8 @@ def kv_attn_append(k_new, v_new, k_cache, v_cache, block_table, positions, *, nu
     p = make_params(batch=B, num_q_heads=num_kv_heads, num_kv_heads=num_kv_heads, head_dim=d,
                     block_size=block_size, max_ctx_len=0, num_blocks=num_blocks, k_strides=k_strides,
                     v_strides=v_strides, max_blocks_per_seq=max_blocks,
-                    kv_dtype=_dtype_code(k_cache.dtype), q_dtype=_dtype_code(k_cache.dtype))
+                    kv_dtype=_dtype_code(k_cache.dtype), q_dtype=_dtype_code(k_cache.dtype),
+                    num_queries=n)
     _check_extent(k_cache, k_strides, num_blocks, block_size, num_kv_heads, d, "k_cache")
     _check_extent(v_cache, v_strides, num_blocks, block_size, num_kv_heads, d, "v_cache")
     st = _lib.kv_attn_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),

@@ -75,6 +75,10 @@ class WorkloadSpec:
     # Sliding window: None attends every position; W >= 1 attends only the first num_sinks and
     # the last W positions of each sequence, and every other position is NaN-poisoned.
     window: Optional[int] = None
+    # Query tokens per sequence (gamma). gamma > 1: q is [B, gamma, h_q, d] and the tokens are
+    # the last gamma cached positions (a speculative draft being checked); the window poisoning
+    # then spares the union of the gamma tokens' windows.
+    num_queries: int = 1
     description: str = ""
 
     @property
@@ -119,7 +123,7 @@ def preset(name: str, **overrides) -> WorkloadSpec:
 @dataclasses.dataclass
 class Workload:
     spec: WorkloadSpec
-    q: torch.Tensor                       # [B, h_q, d]
+    q: torch.Tensor                       # [B, h_q, d], or [B, gamma, h_q, d] when gamma > 1
     k_cache: torch.Tensor                 # storage tensor (layout per spec.layout)
     v_cache: torch.Tensor
     block_table: Optional[torch.Tensor]   # int32 [B, max_blocks] or None (contiguous)
@@ -230,7 +234,8 @@ def make_workload(spec: WorkloadSpec, device="cpu", layer: int = 0) -> Workload:
     B, hq, d = spec.batch, spec.num_q_heads, spec.head_dim
     kv_dt, q_dt = _dtype(spec.kv_dtype), _dtype(spec.q_dtype)
 
-    q = torch.empty((B, hq, d), dtype=q_dt, device=device)
+    q_shape = (B, hq, d) if spec.num_queries <= 1 else (B, spec.num_queries, hq, d)
+    q = torch.empty(q_shape, dtype=q_dt, device=device)
     _fill_normal(q, _generator(seed, 2, device), spec.q_std)
 
     k = torch.empty(shape, dtype=kv_dt, device=device)
@@ -277,13 +282,14 @@ def make_workload(spec: WorkloadSpec, device="cpu", layer: int = 0) -> Workload:
 
 def _poison_outside_window(k, v, kv, vv, spec, ctx_list, table, block_size) -> None:
     """NaN into every position of a windowed sequence that is neither one of its first
-    ``num_sinks`` positions nor one of its last ``window`` positions. Whole blocks of such
-    positions are filled with one indexed fill; the (at most two) blocks cut by an edge slot by
-    slot range."""
+    ``num_sinks`` positions nor one of its last ``window`` positions (with gamma query tokens,
+    the last ``window + gamma - 1``). Whole blocks of such positions are filled with one indexed
+    fill; the (at most two) blocks cut by an edge slot by slot range."""
     nan = float("nan")
     whole = []
+    span = spec.window + max(spec.num_queries, 1) - 1
     for b, length in enumerate(ctx_list):
-        lo, hi = min(spec.num_sinks, length), max(length - spec.window, 0)  # gap [lo, hi)
+        lo, hi = min(spec.num_sinks, length), max(length - span, 0)  # gap [lo, hi)
         if hi <= lo:
             continue
         if table is None:
@@ -342,7 +348,7 @@ def oracle_sample(w: Workload, seqs, kv_heads=None) -> dict:
     if kv_heads is not None:
         g = w.spec.group
         heads = [kvh * g + j for kvh in kv_heads for j in range(g)]
-        q_sel = q_sel[:, heads]
+        q_sel = q_sel[:, heads] if q_sel.dim() == 3 else q_sel[:, :, heads]
     q = _np_storage(q_sel)
     if w.block_table is None:
         idx = torch.tensor(seqs, dtype=torch.int64, device=w.k_cache.device)

@@ -61,7 +61,7 @@ def test_struct_layout_matches_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert K.kv_attn_abi_version() == 2
+    assert K.kv_attn_abi_version() == 3
     for code in range(8):
         s = K.kv_attn_status_string(code)
         assert s and s != "unknown status"
@@ -97,7 +97,7 @@ def test_get_plan_rejects_invalid_params(kw, status):
     assert e.value.status == status
 
 
-@pytest.mark.parametrize("field,value", [("window", -1), ("reserved", 1)])
+@pytest.mark.parametrize("field,value", [("window", -1), ("num_queries", -1)])
 def test_get_plan_rejects_raw_field_values(field, value):
     """Fields the binding never sets this way are still checked by the library."""
     p = _params()
@@ -105,6 +105,37 @@ def test_get_plan_rejects_raw_field_values(field, value):
     with pytest.raises(K.KvAttnError) as e:
         K.kv_attn_get_plan(p, 256)
     assert e.value.status == K.KV_ATTN_ERR_VALUE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(num_queries=17),                                   # more than 16 query tokens
+    dict(num_queries=4, q_dtype=K.KV_ATTN_F32),             # rows mode is bf16 only
+    dict(num_queries=4, kv_dtype=K.KV_ATTN_F32, k_strides=(8 * 16 * 128, 128, 16 * 128)),
+    dict(num_queries=9),                                    # 9 tokens x group 4 = 36 rows > 32
+    dict(num_queries=3, num_q_heads=8 * 16),                # 3 x 16 = 48 rows > 32
+])
+def test_unsupported_query_token_counts(kw):
+    p = _params(**kw)
+    with pytest.raises(K.KvAttnError) as e:
+        K.kv_attn_get_plan(p, 256)
+    assert e.value.status == K.KV_ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("nq,hq,hkv", [(2, 32, 8), (4, 32, 8), (8, 32, 8), (4, 64, 8), (16, 8, 8)])
+def test_plan_with_several_query_tokens(nq, hq, hkv):
+    """gamma query tokens: matrix-core variant, merge rows and workspace scale with gamma."""
+    B, T = 4, 8192
+    p = _params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
+                max_blocks_per_seq=T // 16, num_blocks=10**6, num_queries=nq)
+    plan = K.kv_attn_get_plan(p, 256)
+    one = K.kv_attn_get_plan(_params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
+                                     max_blocks_per_seq=T // 16, num_blocks=10**6), 256)
+    assert plan["kernel_variant"] == 2
+    assert (plan["num_splits"], plan["split_len"]) == (one["num_splits"], one["split_len"])
+    S = plan["num_splits"]
+    if S > 1:
+        assert plan["grid_merge"] == B * nq * hq
+        assert plan["workspace_bytes"] >= B * nq * hq * S * (128 + 2) * 4
 
 
 def test_binding_rejects_a_window_below_one():
