@@ -21,6 +21,9 @@ with events, never time host submission):
     that duration (the merge launches follow outside the events);
   * with --window W, only the attended positions (the first sinks and the last W) count as
     bytes, both in value and in roofline.achieved;
+  * with --gamma G (speculative-decoding verification) every sequence has G query tokens, the
+    last G cached positions, each attending to its own prefix; bytes count the union of the
+    positions they attend (each KV element once) and tokens_per_s counts B * G tokens;
   * cpu_baseline: the fp64 oracle (oracle/) timed on the host on a bounded sample of the same
     workload (whole (layer, sequence, KV head) units in order, about 15 s of CPU work).
 
@@ -30,6 +33,7 @@ Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -85,6 +89,9 @@ def parse_args():
     ap.add_argument("--attn-sinks", type=int, default=None,
                     help="with --window: leading positions always attended (default: the "
                          "workload's sink count)")
+    ap.add_argument("--gamma", type=int, default=1,
+                    help="query tokens per sequence (speculative-decoding verification: the last "
+                         "gamma cached positions, causal among themselves)")
     ap.add_argument("--eager", action="store_true",
                     help="pass B: launch the split kernels from the host instead of replaying a "
                          "captured HIP graph")
@@ -126,6 +133,12 @@ def main():
     elif args.attn_sinks is not None:
         print("bench.py: --attn-sinks needs --window", file=sys.stderr)
         sys.exit(2)
+    if args.gamma < 1:
+        print("bench.py: --gamma must be >= 1", file=sys.stderr)
+        sys.exit(2)
+    if args.gamma > 1:
+        spec = dataclasses.replace(spec, num_queries=args.gamma)
+        tag = f"{tag}_g{args.gamma}"
     layers = spec.layers
     print(f"[bench] building {args.config} ({layers} layer(s)) on the GPU", file=sys.stderr, flush=True)
     wls = [W.make_workload(spec, device="cuda", layer=l) for l in range(layers)]
@@ -137,10 +150,12 @@ def main():
     elem = 2 if spec.kv_dtype == "bf16" else 4
     lens = [int(x) for x in wls[0].ctx_lens.cpu().tolist()]
     # Algorithmic bytes: the KV of the positions attended (all of them without a window).
-    att = [A.attended_length(t, spec.window, spec.num_sinks) for t in lens]
+    gamma = args.gamma
+    att = [A.attended_length(t, spec.window, spec.num_sinks, gamma) for t in lens]
     kv_bytes_layer = A.unique_kv_read_bytes(att, spec.num_kv_heads, spec.head_dim, elem)
     kv_bytes_step = kv_bytes_layer * layers
-    flops_step = A.decode_attention_flops(att, spec.num_q_heads, spec.head_dim) * layers
+    flops_step = layers * sum(A.verify_attention_flops(t, spec.num_q_heads, spec.head_dim, gamma,
+                                                       spec.window, spec.num_sinks) for t in lens)
 
     calib = None
     if args.calib_copy_mib:
@@ -149,10 +164,11 @@ def main():
                  torch.empty(n, dtype=torch.uint8, device="cuda"))
 
     news = []
-    if args.append:  # the current token's K/V row for every layer (written at ctx_lens[b] - 1)
+    if args.append:  # the current token's K/V rows for every layer (at ctx_lens[b] - gamma ..)
         g = torch.Generator(device="cuda").manual_seed(4242)
         for w in wls:
-            shape = (spec.batch, spec.num_kv_heads, spec.head_dim)
+            shape = ((spec.batch, spec.num_kv_heads, spec.head_dim) if gamma == 1
+                     else (spec.batch, gamma, spec.num_kv_heads, spec.head_dim))
             news.append(tuple(torch.randn(shape, generator=g, device="cuda").to(w.k_cache.dtype)
                               for _ in range(2)))
 
@@ -234,7 +250,7 @@ def main():
 
     append_info = None
     if args.append:  # the append kernel alone, launched back to back
-        positions = [(w.ctx_lens - 1).to(torch.int32) for w in wls]
+        positions = [(w.ctx_lens - gamma).to(torch.int32) for w in wls]
         ks_vs = [w.kv_strides() for w in wls]
 
         def append_all():
@@ -266,7 +282,7 @@ def main():
         b.record()
         torch.cuda.synchronize()
         n = reps * args.steps * len(wls)
-        row_bytes = spec.batch * spec.num_kv_heads * spec.head_dim * elem
+        row_bytes = spec.batch * gamma * spec.num_kv_heads * spec.head_dim * elem
         append_info = {"avg_launch_us": round(a.elapsed_time(b) * 1e3 / n, 3), "timed_by": "HIP graph replay",
                        "bytes_written_per_launch": 2 * row_bytes,
                        "bytes_read_per_launch": 2 * row_bytes, "launches_timed": n}
@@ -295,7 +311,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
-        "tokens_per_s": round(A.aggregate_tokens_per_s(spec.batch, ms_per_step * 1e-3), 1),
+        "tokens_per_s": round(A.aggregate_tokens_per_s(spec.batch * gamma, ms_per_step * 1e-3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -304,7 +320,10 @@ def main():
         "config": {
             "workload": f"{spec.name}: {spec.description}" + (
                 f"; sliding window of {spec.window} positions plus the first {spec.num_sinks} "
-                "(attention sinks), the rest NaN-poisoned and never read" if spec.window else ""),
+                "(attention sinks), the rest NaN-poisoned and never read" if spec.window else "")
+                + (f"; {gamma} query tokens per sequence (speculative-decoding verification: the "
+                   "last gamma cached positions, causal among themselves)" if gamma > 1 else ""),
+            "num_queries": gamma,
             "batch": spec.batch, "num_q_heads": spec.num_q_heads, "num_kv_heads": spec.num_kv_heads,
             "head_dim": spec.head_dim, "max_ctx_len": max(lens), "sum_ctx_len": sum(lens),
             "window": spec.window, "attn_sinks": spec.num_sinks if spec.window else None,
@@ -334,7 +353,9 @@ def main():
         "cpu_baseline": cpu,
     }
     if args.append:
-        line["config"]["append"] = "each layer appends the current token's K/V before attending"
+        line["config"]["append"] = ("each layer appends the current token's K/V before attending"
+                                    if gamma == 1 else
+                                    f"each layer appends the {gamma} draft tokens' K/V before attending")
         line["append"] = append_info
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
@@ -355,8 +376,9 @@ def cpu_baseline(wls, spec, budget_s, elem, A):
     order, until the time budget is spent (at least one unit). Host copies of each unit are made
     outside the timed region. Returns the oracle's unique-KV GB/s."""
     from kv_cache_decode_split_amd import workloads as W
-    from oracle import decode_attention
+    from oracle import decode_attention, verify_attention
 
+    gamma = max(spec.num_queries, 1)
     units = [(l, b, h) for l in range(len(wls)) for b in range(spec.batch)
              for h in range(spec.num_kv_heads)]
     lens = [w.ctx_lens.cpu().tolist() for w in wls]
@@ -364,11 +386,13 @@ def cpu_baseline(wls, spec, budget_s, elem, A):
     for l, b, h in units:
         v = W.oracle_sample(wls[l], [b], [h])
         t0 = time.perf_counter()
-        decode_attention(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
-                         block_size=v["block_size"] if v["block_table"] is not None else None,
-                         window=spec.window, num_sinks=spec.num_sinks)
+        fn = decode_attention if gamma == 1 else verify_attention
+        fn(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
+           block_size=v["block_size"] if v["block_table"] is not None else None,
+           window=spec.window, num_sinks=spec.num_sinks)
         spent += time.perf_counter() - t0
-        done_bytes += 2 * A.attended_length(lens[l][b], spec.window, spec.num_sinks) * spec.head_dim * elem
+        done_bytes += 2 * A.attended_length(lens[l][b], spec.window, spec.num_sinks,
+                                            gamma) * spec.head_dim * elem
         n += 1
         if spent >= budget_s:
             break

@@ -29,6 +29,7 @@ from typing import Iterable, Union
 
 __all__ = [
     "attended_length",
+    "verify_attention_flops",
     "MI355X_HBM_PEAK_GBPS",
     "kv_cache_bytes_eq3",
     "kv_bytes_per_token",
@@ -73,14 +74,33 @@ def unique_kv_bytes_per_position(num_kv_heads: int, head_dim: int, elem_bytes: i
     return 2 * num_kv_heads * head_dim * elem_bytes
 
 
-def attended_length(length: int, window: int | None = None, num_sinks: int = 0) -> int:
+def attended_length(length: int, window: int | None = None, num_sinks: int = 0,
+                    num_queries: int = 1) -> int:
     """Positions a decode step attends to in a sequence of ``length`` positions: all of them, or
     with a window W the union of the first ``num_sinks`` and the last W positions (Ch. 19 §19.4.3
-    sliding window with attention sinks). These are the positions whose KV the step reads."""
+    sliding window with attention sinks). These are the positions whose KV the step reads.
+
+    With ``num_queries`` = γ query tokens (the last γ positions, each attending to its own
+    prefix, Ch. 19 §19.8) the count is that of the union of the γ tokens' positions: with a
+    window, the first ``num_sinks`` and the last W + γ - 1 positions."""
     length = max(int(length), 0)
     if window is None:
         return length
-    return min(length, min(int(num_sinks), length) + min(int(window), length))
+    span = int(window) + max(int(num_queries), 1) - 1
+    return min(length, min(int(num_sinks), length) + min(span, length))
+
+
+def verify_attention_flops(length: int, num_q_heads: int, head_dim: int, num_queries: int,
+                           window: int | None = None, num_sinks: int = 0) -> int:
+    """FLOPs of the γ query tokens of one sequence of ``length`` cached positions: token j
+    attends to the first length - γ + 1 + j positions (windowed as for one token), at
+    4 · h_q · d FLOPs per attended position (QKᵀ and PV, 2 FLOPs per multiply-add)."""
+    total = 0
+    for j in range(num_queries):
+        visible = int(length) - num_queries + 1 + j
+        if visible > 0:
+            total += attended_length(visible, window, num_sinks)
+    return 4 * num_q_heads * head_dim * total
 
 
 def unique_kv_read_bytes(lengths: Lengths, num_kv_heads: int, head_dim: int, elem_bytes: int,

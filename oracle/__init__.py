@@ -22,6 +22,9 @@ kv_append
 verify_attention
     γ new query tokens per sequence attending causally among themselves (the target model's
     check of a speculative-decoding draft).
+evict_select
+    Budgeted KV eviction selection: the current position of every (layer, head) kept, the rest
+    ranked in one global pool by (−score, layer, head, token) and the first M − L·H kept.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed forms, invariants,
 brute force and the independent pure-Python implementation (no function is "parity unpinned").
@@ -47,3 +50,4 @@ from .online_softmax import (  # noqa: F401
 from .fsum_reference import decode_attention_fsum  # noqa: F401
 from .kv_append import append_kv  # noqa: F401
 from .verify_attention import verify_attention  # noqa: F401
+from .evict_select import evict_select  # noqa: F401

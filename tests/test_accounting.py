@@ -2,6 +2,8 @@
 
 import json
 import math
+
+import numpy as np
 import os
 
 import pytest
@@ -119,3 +121,33 @@ def test_attended_length_counts_the_oracle_positions():
             for sinks in (0, 1, 4, 50, 10000):
                 want = len(attended_positions(length, window, sinks))
                 assert A.attended_length(length, window, sinks) == want, (length, window, sinks)
+
+
+def test_attended_length_of_several_tokens_counts_the_union_of_their_positions():
+    """With γ query tokens the byte count is the size of the union of the positions the oracle's
+    γ tokens attend (token j: the attended positions of the first T - γ + 1 + j)."""
+    from oracle import attended_positions
+    for length in (0, 1, 3, 16, 17, 100, 700):
+        for gamma in (1, 2, 4, 16):
+            for window in (None, 1, 3, 16, 64, 5000):
+                for sinks in (0, 4, 50):
+                    union = set()
+                    for j in range(gamma):
+                        visible = length - gamma + 1 + j
+                        if visible > 0:
+                            union |= set(np.asarray(attended_positions(visible, window, sinks)).tolist())
+                    got = A.attended_length(length, window, sinks, num_queries=gamma)
+                    assert got == len(union), (length, gamma, window, sinks)
+
+
+def test_verify_flops_sum_the_tokens_visible_positions():
+    from oracle import attended_positions
+    for length, gamma, window, sinks in [(100, 4, None, 0), (3, 8, None, 0), (700, 4, 64, 4)]:
+        want = 0
+        for j in range(gamma):
+            visible = length - gamma + 1 + j
+            if visible > 0:
+                want += len(attended_positions(visible, window, sinks))
+        assert A.verify_attention_flops(length, 32, 128, gamma, window, sinks) == 4 * 32 * 128 * want
+    # one token is the single-token count
+    assert A.verify_attention_flops(4096, 32, 128, 1) == A.decode_attention_flops([4096], 32, 128)
