@@ -45,6 +45,8 @@ __all__ = [
     "workload_structure",
     "oracle_view",
     "oracle_sample",
+    "EVICT_PRESETS",
+    "make_scores",
 ]
 
 # Elements per random draw; fixed so that a seed gives the same bytes on every run.
@@ -384,3 +386,49 @@ def oracle_sample(w: Workload, seqs, kv_heads=None) -> dict:
                 ctx_lens=ctx[seqs].numpy().astype(np.int64), block_table=table,
                 block_size=w.block_size)
 
+
+
+# ---- scores for the budgeted eviction selection -----------------------------------------------
+#
+# Eviction ranks (layer, KV head, position) entries by an attention score. The scores are drawn
+# directly (nothing here computes attention): "lognormal" draws exp(sigma * z), z ~ N(0, 1), a
+# positive, heavy-tailed spread over orders of magnitude with a few large "heavy hitters", the
+# shape of accumulated attention mass; "levels" draws from a handful of values (heavy ties, so the
+# (layer, head, position) tie-break decides many entries); "normal" draws z itself (signs and
+# zeros mixed); "equal" gives every entry the same score (every entry ties).
+
+EVICT_PRESETS = {
+    # LLaMA-7B-shaped model (32 layers, 32 KV heads) at the 4096-token context of C2.
+    "E1": dict(num_layers=32, num_heads=32, num_tokens=4096, budget_frac=0.25, kind="lognormal",
+               sigma=2.0, seed=2001),
+    # The long-context shape of C5 (8 KV heads, 131072 positions) over 32 layers.
+    "E2": dict(num_layers=32, num_heads=8, num_tokens=131072, budget_frac=0.10, kind="lognormal",
+               sigma=2.0, seed=2002),
+}
+
+
+def make_scores(num_layers: int, num_heads: int, num_tokens: int, kind: str = "lognormal",
+                seed: int = 0, device="cpu", sigma: float = 2.0, row_stride: Optional[int] = None,
+                levels=(0.0, 0.25, 0.5, 1.0)) -> torch.Tensor:
+    """Seeded fp32 scores [L, H, N] (a view with rows ``row_stride`` apart when given)."""
+    stride = num_tokens if row_stride is None else int(row_stride)
+    if stride < num_tokens:
+        raise ValueError("row_stride < num_tokens")
+    rows = num_layers * num_heads
+    store = torch.empty((rows, stride), dtype=torch.float32, device=device)
+    gen = _generator(seed, 6, device)
+    if kind in ("lognormal", "normal"):
+        _fill_normal(store, gen, 1.0)
+        if kind == "lognormal":
+            store.mul_(sigma).exp_()
+    elif kind == "levels":
+        idx = torch.randint(0, len(levels), (rows, stride), generator=gen, device=device)
+        store.copy_(torch.tensor(list(levels), dtype=torch.float32, device=device)[idx])
+    elif kind == "equal":
+        store.fill_(1.0)
+    else:
+        raise ValueError(f"unknown score kind {kind!r}")
+    if stride > num_tokens:
+        store[:, num_tokens:] = float("nan")  # never read
+    return store[:, :num_tokens].view(num_layers, num_heads, num_tokens) if stride == num_tokens \
+        else store.view(num_layers, num_heads, stride)[:, :, :num_tokens]
