@@ -92,6 +92,9 @@ def parse_args():
     ap.add_argument("--gamma", type=int, default=1,
                     help="query tokens per sequence (speculative-decoding verification: the last "
                          "gamma cached positions, causal among themselves)")
+    ap.add_argument("--evict", choices=["E1", "E2"], default=None,
+                    help="time the budgeted eviction selection on this score workload instead of "
+                         "decode attention")
     ap.add_argument("--eager", action="store_true",
                     help="pass B: launch the split kernels from the host instead of replaying a "
                          "captured HIP graph")
@@ -121,6 +124,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.evict is not None:
+        bench_evict(args, W)
+        return
     spec = W.PRESETS[args.config]
     tag = args.config
     if args.window is not None:
@@ -359,6 +365,117 @@ def main():
         line["append"] = append_info
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
+    print(json.dumps(line), flush=True)
+
+
+def bench_evict(args, W):
+    """Budgeted eviction selection (kv_evict_select) on a seeded score workload.
+
+    One call is the whole selection (all its launches). Algorithmic bytes per call: every score
+    read once (4 bytes) and every mask byte written once; the calls are captured in a HIP graph
+    and replayed back to back between device events."""
+    import numpy as np
+    import torch
+
+    from kv_cache_decode_split_amd import kv_evict as E
+
+    cfg = W.EVICT_PRESETS[args.evict]
+    L, H, N = cfg["num_layers"], cfg["num_heads"], cfg["num_tokens"]
+    n = L * H * N
+    budget = int(cfg["budget_frac"] * n)
+    print(f"[bench] building {args.evict} scores ({L}x{H}x{N}) on the GPU", file=sys.stderr, flush=True)
+    scores = W.make_scores(L, H, N, cfg["kind"], seed=cfg["seed"], device="cuda", sigma=cfg["sigma"])
+    keep = torch.empty((L, H, N), dtype=torch.uint8, device="cuda")
+    p = E.make_evict_params(L, H, N, budget)
+    ws = torch.empty(max(E.kv_evict_workspace_size(p), 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        E.kv_evict_select(scores, budget, keep=keep, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    warmup = args.warmup if args.warmup is not None else 20
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / args.steps
+    kept = int(keep.sum().item())
+    alg_bytes = 5 * n
+    achieved = alg_bytes / (us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import evict_select
+        host = scores.cpu().numpy()
+        layers, spent = L, 0.0
+        while True:  # the oracle on the first `layers` layers, shrunk until it fits the budget
+            t0 = time.perf_counter()
+            evict_select(host[:layers], int(cfg["budget_frac"] * layers * H * N))
+            spent = time.perf_counter() - t0
+            if spent <= args.cpu_seconds or layers == 1:
+                break
+            layers = max(1, int(layers * args.cpu_seconds / spent / 2))
+        cpu = {"value": round(5 * layers * H * N / spent / 1e9, 4), "unit": "GB/s",
+               "cores": _blas_threads(), "kind": "oracle",
+               "sample": f"the first {layers} of {L} layers ({layers * H * N} entries, budget "
+                         f"fraction {cfg['budget_frac']}), {spent:.1f} s of oracle time"}
+    line = {
+        "metric": "eviction selection: achieved HBM GB/s (score bytes read + mask bytes written "
+                  "/ time) + µs/call",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warmup,
+        "ms_per_step": round(us * 1e-3, 5),
+        "us_per_step": round(us, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.evict}: budgeted KV eviction selection over L={L} layers x H={H} "
+                        f"KV heads x N={N} positions ({n} entries), scores {cfg['kind']} "
+                        f"(sigma {cfg['sigma']}), budget M = {budget} ({cfg['budget_frac']:.0%}), "
+                        "current position N-1",
+            "num_layers": L, "num_heads": H, "num_tokens": N, "budget": budget,
+            "entries_kept": kept,
+            "algorithmic_bytes_per_call": alg_bytes,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kv_evict_select (whole call: init, two streaming passes, list passes, patch)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_us": round(us, 2),
+            "launches_timed": args.steps,
+            "timed_by": "HIP graph replay",
+        },
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(line), flush=True)
 
 

@@ -16,7 +16,7 @@
  * of the (M - L*H)-th largest 64-bit key (score bits made order-preserving, then the complement
  * of the flat index (l*H + h)*N + t, so that ties fall to the lower index): two streaming passes
  * over the scores (a histogram of the top digit; then the mask, with the entries of the
- * boundary digit set aside), then a few passes over the set-aside entries only.
+ * boundary digit set aside), then passes over the set-aside entries only.
  *
  * Readings where the page is silent: scores compare as values (-0.0 ties with +0.0, +-inf are
  * allowed, NaN is outside the contract); C is one position shared by every row; when
@@ -46,8 +46,9 @@ typedef struct kv_evict_params {
 
 /*
  * Workspace bytes kv_evict_select needs for `p`: 0 when the budget alone decides the result
- * (M - L*H <= 0, or M - L*H >= L*H*(N - 1)), otherwise 164096 bytes of selection state and
- * histograms plus 8 bytes per pool entry (L*H*(N - 1)). Returns 0 for invalid `p` as well.
+ * (M - L*H <= 0, or M - L*H >= L*H*(N - 1)), otherwise 397568 bytes of selection state and
+ * histograms plus two candidate lists of 8 bytes per slot, each with at least L*H*N slots
+ * (rounded up to whole blocks of 16384 entries per workgroup). Returns 0 for invalid `p`.
  */
 size_t kv_evict_workspace_size(const kv_evict_params* p);
 

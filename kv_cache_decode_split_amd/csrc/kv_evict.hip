@@ -9,22 +9,29 @@
 // set on the others, -0.0 folded onto +0.0), the low word is the complement of the flat index
 // i = (l*H + h)*N + t, so a lower index wins a tie. The K entries that stay are exactly those
 // whose key is at least k*, the K-th largest key. k* is found digit by digit from the top (a
-// radix selection, five digits of 13, 13, 13, 13 and 12 bits):
+// radix selection, five digits of 13, 13, 13, 13 and 12 bits), with kernel boundaries as the
+// only grid-wide synchronisation:
 //
-//   pass 0  every entry: histogram of the top digit; the last workgroup to finish finds the
-//           digit of k* and the rank of k* among the entries that share it;
-//   pass 1  every entry: writes the whole mask (current positions 1, entries whose top digit is
-//           above k*'s 1, all others 0 for now) and sets the entries that share k*'s top digit
-//           aside (their keys, in a workspace list) while histogramming their second digit;
-//   pass 2-4  the set-aside entries only: one digit each;
-//   patch   the set-aside entries whose key is at least k* get a 1.
+//   init    clears the histograms;
+//   pass0   every entry: histogram of the top digit;
+//   pass1   every workgroup first fixes k*'s top digit from that histogram (the same result in
+//           each), then streams every entry again: writes the whole mask (current positions 1,
+//           entries whose top digit is above k*'s 1, all others 0 for now) and copies the keys
+//           that share k*'s top digit into list 1 (each workgroup into its own region, so no
+//           global counter is needed), with a histogram of their second digit;
+//   list    every workgroup first fixes k*'s second digit from pass 1's histogram, then walks
+//           its share of list 1: entries above k*'s first two digits get a 1, those sharing
+//           them go to list 2 (again one region per workgroup);
+//   final   one workgroup fixes digits 2 to 4 over list 2 with LDS histograms and gives a 1 to
+//           the list-2 entries at or above k*.
 //
 // The two full passes stream the scores with coalesced 128-bit loads (HBM-bound: 8 bytes read
-// and 1 written per entry); the rest touches only the set-aside entries, typically a small
-// fraction of the pool (all of it only if nearly every score is equal). No ranking of the whole
-// pool is ever materialised. Histograms live in LDS per workgroup and are added into global
-// memory with device-scope atomics (bins that stayed zero are skipped); the last workgroup of
-// each pass, detected with an arrival counter, reads the global histogram and fixes the digit.
+// and 1 written per entry); list 1 is typically a small fraction of the pool and list 2 a few
+// entries (all of the pool only if nearly every score is equal, when the single final
+// workgroup becomes the slow part). Histograms are built in LDS per workgroup and added into
+// one of several global replicas with device-scope atomics, skipping bins that stayed zero, so
+// few workgroups contend for one address. No kernel uses a device-scope fence or a grid-wide
+// arrival counter: on this chip each costs tens of nanoseconds per workgroup, serialised.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,40 +43,75 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+#ifndef KV_EVICT_STREAM_THREADS
+#define KV_EVICT_STREAM_THREADS 1024
+#endif
+#ifndef KV_EVICT_SLABS
+#define KV_EVICT_SLABS 4
+#endif
+#ifndef KV_EVICT_GRID
+#define KV_EVICT_GRID 256
+#endif
+#ifndef KV_EVICT_REPLICAS
+#define KV_EVICT_REPLICAS 8
+#endif
+
+constexpr int kStreamThreads = KV_EVICT_STREAM_THREADS;  // threads of a full-pass workgroup
 constexpr int kVec = 4;                              // floats per 128-bit load
-constexpr int kSlabs = 4;                            // loads per thread per iteration
-constexpr int kChunk = kThreads * kVec * kSlabs;     // entries per workgroup iteration
+constexpr int kSlabs = KV_EVICT_SLABS;               // loads per thread per iteration
+constexpr int kChunk = kStreamThreads * kVec * kSlabs;  // entries per workgroup iteration
+constexpr int kGrid = KV_EVICT_GRID;                 // workgroups of the full passes (at most)
+constexpr int kListGrid = 64;                        // workgroups of the list pass (at most)
+constexpr int kFinishThreads = 1024;                 // list-pass and final workgroups
+constexpr int kLdsKeys = 6144;                       // list-2 entries the final kernel stages
 constexpr int kBins = 8192;                          // 13-bit digits
-constexpr int kPasses = 5;
-constexpr int kMaxGrid = 2048;
-constexpr int kListGrid = 256;                       // workgroups of the passes over the list
+constexpr int kReplicas0 = KV_EVICT_REPLICAS;        // copies of the top digit's histogram
+constexpr int kReplicas1 = 4;                        // copies of the second digit's histogram
 constexpr size_t kStateBytes = 256;
-constexpr size_t kHistBytes = size_t(kPasses) * kBins * 4;
+constexpr size_t kHistBytes = size_t(kReplicas0 + kReplicas1) * kBins * 4;
+constexpr size_t kCountBytes = 4096;                 // per-region list-1 and list-2 counts
+constexpr size_t kFixedBytes = kStateBytes + kHistBytes + kCountBytes;
+static_assert((kGrid + kListGrid) * 4 <= int(kCountBytes), "per-region counts");
+static_assert(kBins % kStreamThreads == 0 && kBins % kFinishThreads == 0, "bins per thread");
 
 __host__ __device__ constexpr int digit_shift(int pass) { return pass < 4 ? 51 - 13 * pass : 0; }
 __host__ __device__ constexpr int digit_bits(int pass) { return pass < 4 ? 13 : 12; }
 
 struct State {
-  unsigned long long prefix;     // digits of k* found so far, in place (lower bits 0)
-  unsigned long long k_rem;      // rank of k* (1 = largest) among the keys sharing those digits
-  unsigned int list_count;       // entries set aside by pass 1
-  unsigned int arrived[kPasses]; // workgroups that finished each pass
+  unsigned long long prefix0;    // k*'s top digit, in place (written by pass1)
+  unsigned long long k_rem0;     // rank of k* (1 = largest) among the keys sharing it
+  unsigned long long prefix1;    // k*'s top two digits (written by the list pass)
+  unsigned long long k_rem1;     // rank of k* among the keys sharing them
 };
 static_assert(sizeof(State) <= kStateBytes, "state");
+
+// Sizes that follow from the problem alone (the same on the host and in every kernel).
+struct Geometry {
+  int32_t grid;                  // workgroups of the full passes = list-1 regions
+  int32_t list_grid;             // workgroups of the list pass = list-2 regions
+  int64_t cap1;                  // list-1 entries per region (the entries its workgroup visits)
+  int64_t cap2;                  // list-2 entries per region (the list-1 regions it walks)
+};
 
 struct Args {
   const float* scores;
   uint8_t* keep;
   State* st;
-  unsigned int* hist;            // [kPasses][kBins]
-  unsigned long long* list;      // set-aside keys
+  unsigned int* hist0;           // [kReplicas0][kBins]: top digit over the pool
+  unsigned int* hist1;           // [kReplicas1][kBins]: second digit over list 1
+  unsigned int* count1;          // [grid]: list-1 entries in each region
+  unsigned int* count2;          // [list_grid]: list-2 entries in each region
+  unsigned long long* list1;     // [grid][cap1]
+  unsigned long long* list2;     // [list_grid][cap2]
   int64_t row_stride;
   int64_t n;                     // L*H*N < 2^31
-  unsigned long long magic;      // row of flat index i: (i * magic) >> magic_shift
-  int32_t magic_shift;
+  int64_t cap1, cap2;
+  int32_t grid;
+  int32_t list_grid;
   int32_t N;
   int32_t current;
+  int32_t magic_shift;
+  unsigned long long magic;      // row of flat index i: (i * magic) >> magic_shift
   unsigned long long k;          // K = M - L*H, 1 <= K < pool size
 };
 
@@ -88,14 +130,6 @@ __device__ __forceinline__ int digit_of(unsigned long long key, int pass) {
   return int((key >> digit_shift(pass)) & ((1ull << digit_bits(pass)) - 1ull));
 }
 
-__device__ __forceinline__ void atomic_add_agent(unsigned int* p, unsigned int v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned int load_agent(const unsigned int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Four consecutive entries i0 .. i0+3 (i0 a multiple of 4). VEC: the four share a row and one
 // aligned 128-bit load reads them. valid: inside the array; pool: valid and not the current
 // position.
@@ -105,23 +139,20 @@ __device__ __forceinline__ void load4(const Args& a, int64_t i0, float (&x)[4], 
   if constexpr (VEC) {
     const bool in = i0 < a.n;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) valid[e] = in;
+    for (int e = 0; e < 4; ++e) {
+      valid[e] = in;
+      x[e] = 0.f;
+      pool[e] = false;
+    }
     if (in) {
       const int row = row_of(a, i0);
       const int t0 = int(i0 - int64_t(row) * a.N);
       const f32x4_t v = __builtin_nontemporal_load(
           reinterpret_cast<const f32x4_t*>(a.scores + int64_t(row) * a.row_stride + t0));
-      x[0] = v[0];
-      x[1] = v[1];
-      x[2] = v[2];
-      x[3] = v[3];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pool[e] = t0 + e != a.current;
-    } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = 0.f;
-        pool[e] = false;
+        x[e] = v[e];
+        pool[e] = t0 + e != a.current;
       }
     }
   } else {
@@ -141,7 +172,36 @@ __device__ __forceinline__ void load4(const Args& a, int64_t i0, float (&x)[4], 
   }
 }
 
-// Exclusive prefix sum over the workgroup's threads, in thread order.
+// Add a workgroup's LDS histogram into one replica of a global histogram (bins that stayed zero
+// are skipped, so a workgroup touches only the bins its entries fell into).
+template <int THREADS>
+__device__ __forceinline__ void flush_hist(const unsigned int* h_lds, unsigned int* h_glob) {
+  for (int i = threadIdx.x; i < kBins; i += THREADS) {
+    const unsigned int c = h_lds[i];
+    if (c != 0u) __hip_atomic_fetch_add(h_glob + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// s_tot[b] = sum over the R replicas of bin b, with every load issued before any is used.
+template <int R, int THREADS>
+__device__ __forceinline__ void sum_replicas(const unsigned int* h, unsigned int* s_tot) {
+  constexpr int PER = kBins / THREADS;
+  unsigned int v[PER][R];
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[j][r] = h[size_t(r) * kBins + j * THREADS + threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    unsigned int t = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) t += v[j][r];
+    s_tot[j * THREADS + threadIdx.x] = t;
+  }
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order (s_wave: THREADS/64 words).
+template <int THREADS>
 __device__ __forceinline__ unsigned int block_exclusive_scan(unsigned int x, unsigned int* s_wave) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -159,168 +219,221 @@ __device__ __forceinline__ unsigned int block_exclusive_scan(unsigned int x, uns
   return base + inc - x;
 }
 
-// Run by the whole last workgroup of a pass: the digit of k* is the bin, scanned from the top,
-// in which the running count first reaches k_rem.
-__device__ void find_digit(const Args& a, int pass) {
-  __shared__ unsigned int s_wave[kThreads / 64];
-  const unsigned int* h = a.hist + size_t(pass) * kBins;
+// Given the histogram of digit `pass` over the keys that share k*'s higher digits (s_tot, in
+// LDS), fix that digit: it is the bin, scanned from the top, in which the running count first
+// reaches k_rem. Updates *prefix and *k_rem (LDS) for the whole workgroup.
+template <int THREADS>
+__device__ void select_digit(const unsigned int* s_tot, int pass, unsigned long long* prefix,
+                             unsigned long long* k_rem) {
+  __shared__ unsigned int s_wave[THREADS / 64];
   const int nb = 1 << digit_bits(pass);
-  const int per = nb / kThreads;
+  const int per = nb / THREADS;
   const int first = nb - 1 - int(threadIdx.x) * per;  // this thread's bins: first, first-1, ...
   unsigned int local = 0;
-  for (int j = 0; j < per; ++j) local += load_agent(h + (first - j));
-  const unsigned int before = block_exclusive_scan(local, s_wave);
-  const unsigned long long k = a.st->k_rem;
+  for (int j = 0; j < per; ++j) local += s_tot[first - j];
+  const unsigned int before = block_exclusive_scan<THREADS>(local, s_wave);
+  const unsigned long long k = *k_rem;
+  __syncthreads();
   if (before < k && k <= static_cast<unsigned long long>(before) + local) {
     unsigned long long acc = before;
     for (int j = 0; j < per; ++j) {
-      const unsigned int c = load_agent(h + (first - j));
+      const unsigned int c = s_tot[first - j];
       if (k <= acc + c) {
-        a.st->prefix |= static_cast<unsigned long long>(first - j) << digit_shift(pass);
-        a.st->k_rem = k - acc;
+        *prefix |= static_cast<unsigned long long>(first - j) << digit_shift(pass);
+        *k_rem = k - acc;
         break;
       }
       acc += c;
     }
   }
-}
-
-// End of a histogram pass: publish this workgroup's counts, count arrivals; the last workgroup
-// to arrive fixes the digit.
-__device__ void finish_pass(const Args& a, int pass, const unsigned int* h_lds) {
-  __shared__ unsigned int s_last;
-  unsigned int* h = a.hist + size_t(pass) * kBins;
-  const int nb = 1 << digit_bits(pass);
-  for (int i = threadIdx.x; i < nb; i += kThreads) {
-    const unsigned int c = h_lds[i];
-    if (c != 0u) atomic_add_agent(h + i, c);
-  }
-  __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned int prev =
-        __hip_atomic_fetch_add(&a.st->arrived[pass], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == gridDim.x - 1 ? 1u : 0u;
-  }
-  __syncthreads();
-  if (s_last == 0u) return;
-  __threadfence();
-  find_digit(a, pass);
 }
 
-__global__ __launch_bounds__(kThreads) void init_kernel(const Args a) {
-  const int i = int(blockIdx.x) * kThreads + int(threadIdx.x);
-  if (i < kPasses * kBins) a.hist[i] = 0u;
-  if (i == 0) {
-    a.st->prefix = 0ull;
-    a.st->k_rem = a.k;
-    a.st->list_count = 0u;
-    for (int p = 0; p < kPasses; ++p) a.st->arrived[p] = 0u;
-  }
+__global__ __launch_bounds__(256) void init_kernel(const Args a) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);  // one 16-byte piece
+  constexpr int kPieces = (kReplicas0 + kReplicas1) * kBins / 4;
+  if (i < kPieces) reinterpret_cast<u32x4_t*>(a.hist0)[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
+// Pass 0: histogram of the top digit over the whole pool.
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void pass0_kernel(const Args a) {
+__global__ __launch_bounds__(kStreamThreads) void pass0_kernel(const Args a) {
   __shared__ unsigned int h[kBins];
-  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
+  for (int i = threadIdx.x; i < kBins; i += kStreamThreads) h[i] = 0u;
   __syncthreads();
   for (int64_t base = int64_t(blockIdx.x) * kChunk; base < a.n; base += int64_t(gridDim.x) * kChunk) {
+    float x[kSlabs][4];
+    bool valid[kSlabs][4], pool[kSlabs][4];
+#pragma unroll
+    for (int s = 0; s < kSlabs; ++s)
+      load4<VEC>(a, base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec, x[s], valid[s], pool[s]);
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
-      const int64_t i0 = base + s * (kThreads * kVec) + int(threadIdx.x) * kVec;
-      float x[4];
-      bool valid[4], pool[4];
-      load4<VEC>(a, i0, x, valid, pool);
+      const int64_t i0 = base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (pool[e]) atomicAdd(&h[digit_of(make_key(x[e], uint32_t(i0 + e)), 0)], 1u);
+        if (pool[s][e]) atomicAdd(&h[digit_of(make_key(x[s][e], uint32_t(i0 + e)), 0)], 1u);
     }
   }
   __syncthreads();
-  finish_pass(a, 0, h);
+  flush_hist<kStreamThreads>(h, a.hist0 + size_t(blockIdx.x % kReplicas0) * kBins);
 }
 
+// Pass 1: fixes k*'s top digit (every workgroup, identically), then the whole mask, list 1 in
+// this workgroup's region and the histogram of the second digit over it.
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void pass1_kernel(const Args a) {
+__global__ __launch_bounds__(kStreamThreads) void pass1_kernel(const Args a) {
   __shared__ unsigned int h[kBins];
-  __shared__ unsigned long long s_list[kChunk];
-  __shared__ unsigned int s_n, s_base;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
-  const int d0 = digit_of(a.st->prefix, 0);
+  __shared__ unsigned long long s_prefix, s_k;
+  __shared__ unsigned int s_n;
+  sum_replicas<kReplicas0, kStreamThreads>(a.hist0, h);
+  if (threadIdx.x == 0) {
+    s_prefix = 0ull;
+    s_k = a.k;
+    s_n = 0u;
+  }
+  __syncthreads();
+  select_digit<kStreamThreads>(h, 0, &s_prefix, &s_k);
+  const int d0 = digit_of(s_prefix, 0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.st->prefix0 = s_prefix;
+    a.st->k_rem0 = s_k;
+  }
+  for (int i = threadIdx.x; i < kBins; i += kStreamThreads) h[i] = 0u;
+  __syncthreads();
+  unsigned long long* region = a.list1 + int64_t(blockIdx.x) * a.cap1;
   for (int64_t base = int64_t(blockIdx.x) * kChunk; base < a.n; base += int64_t(gridDim.x) * kChunk) {
-    if (threadIdx.x == 0) s_n = 0u;
-    __syncthreads();
+    float x[kSlabs][4];
+    bool valid[kSlabs][4], pool[kSlabs][4];
+#pragma unroll
+    for (int s = 0; s < kSlabs; ++s)
+      load4<VEC>(a, base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec, x[s], valid[s], pool[s]);
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
-      const int64_t i0 = base + s * (kThreads * kVec) + int(threadIdx.x) * kVec;
-      float x[4];
-      bool valid[4], pool[4];
-      load4<VEC>(a, i0, x, valid, pool);
+      const int64_t i0 = base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec;
       uint32_t m[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m[e] = valid[e] ? 1u : 0u;  // current positions stay
-        if (pool[e]) {
-          const unsigned long long key = make_key(x[e], uint32_t(i0 + e));
+        m[e] = valid[s][e] ? 1u : 0u;  // current positions stay
+        if (pool[s][e]) {
+          const unsigned long long key = make_key(x[s][e], uint32_t(i0 + e));
           const int d = digit_of(key, 0);
           m[e] = d > d0 ? 1u : 0u;
           if (d == d0) {
-            const unsigned int pos = atomicAdd(&s_n, 1u);
-            s_list[pos] = key;
+            region[atomicAdd(&s_n, 1u)] = key;
             atomicAdd(&h[digit_of(key, 1)], 1u);
           }
         }
       }
       if constexpr (VEC) {
-        if (valid[0])
+        if (valid[s][0])
           *reinterpret_cast<uint32_t*>(a.keep + i0) = m[0] | (m[1] << 8) | (m[2] << 16) | (m[3] << 24);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (valid[e]) a.keep[i0 + e] = uint8_t(m[e]);
+          if (valid[s][e]) a.keep[i0 + e] = uint8_t(m[e]);
       }
     }
-    __syncthreads();
-    if (threadIdx.x == 0 && s_n != 0u)
-      s_base = __hip_atomic_fetch_add(&a.st->list_count, s_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    for (unsigned int j = threadIdx.x; j < s_n; j += kThreads) a.list[s_base + j] = s_list[j];
-    __syncthreads();
   }
   __syncthreads();
-  finish_pass(a, 1, h);
+  if (threadIdx.x == 0) a.count1[blockIdx.x] = s_n;
+  flush_hist<kStreamThreads>(h, a.hist1 + size_t(blockIdx.x % kReplicas1) * kBins);
 }
 
-// Passes 2..4: histogram of digit `pass` over the set-aside keys that still share k*'s digits.
-__global__ __launch_bounds__(kThreads) void list_pass_kernel(const Args a, int pass) {
-  __shared__ unsigned int h[kBins];
-  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
-  __syncthreads();
-  const int sh = digit_shift(pass - 1);
-  const unsigned long long want = a.st->prefix >> sh;
-  const unsigned int count = a.st->list_count;
-  for (unsigned int j = blockIdx.x * kThreads + threadIdx.x; j < count; j += gridDim.x * kThreads) {
-    const unsigned long long key = a.list[j];
-    if ((key >> sh) == want) atomicAdd(&h[digit_of(key, pass)], 1u);
+// List pass: every workgroup fixes k*'s second digit (identically), then walks the list-1
+// regions r = blockIdx.x, blockIdx.x + gridDim.x, ...: entries above k*'s first two digits get
+// a 1, entries sharing them go to this workgroup's list-2 region.
+__global__ __launch_bounds__(kFinishThreads) void list_kernel(const Args a) {
+  __shared__ unsigned int s_tot[kBins];
+  __shared__ unsigned long long s_prefix, s_k;
+  __shared__ unsigned int s_n;
+  sum_replicas<kReplicas1, kFinishThreads>(a.hist1, s_tot);
+  if (threadIdx.x == 0) {
+    s_prefix = a.st->prefix0;
+    s_k = a.st->k_rem0;
+    s_n = 0u;
   }
   __syncthreads();
-  finish_pass(a, pass, h);
+  select_digit<kFinishThreads>(s_tot, 1, &s_prefix, &s_k);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.st->prefix1 = s_prefix;
+    a.st->k_rem1 = s_k;
+  }
+  const unsigned long long want = s_prefix >> digit_shift(1);
+  unsigned long long* region = a.list2 + int64_t(blockIdx.x) * a.cap2;
+  for (int r = blockIdx.x; r < a.grid; r += gridDim.x) {
+    const unsigned int count = a.count1[r];
+    const unsigned long long* src = a.list1 + int64_t(r) * a.cap1;
+    for (unsigned int j = threadIdx.x; j < count; j += kFinishThreads) {
+      const unsigned long long key = src[j];
+      const unsigned long long top = key >> digit_shift(1);
+      if (top > want)
+        a.keep[~static_cast<uint32_t>(key)] = 1u;
+      else if (top == want)
+        region[atomicAdd(&s_n, 1u)] = key;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.count2[blockIdx.x] = s_n;
 }
 
-// The set-aside entries at or above k* stay.
-__global__ __launch_bounds__(kThreads) void patch_kernel(const Args a) {
-  const unsigned long long kstar = a.st->prefix;
-  const unsigned int count = a.st->list_count;
-  for (unsigned int j = blockIdx.x * kThreads + threadIdx.x; j < count; j += gridDim.x * kThreads) {
-    const unsigned long long key = a.list[j];
+// One workgroup finishes: digits 2 to 4 over list 2 (LDS histograms), then the list-2 entries
+// at or above k* get a 1. List 2 is visited as one concatenated array: entry j lives in the
+// region r with s_offs[r] <= j < s_offs[r + 1]; when it fits, it is first copied into LDS so
+// that the three digit passes do not wait on global memory.
+__global__ __launch_bounds__(kFinishThreads) void final_kernel(const Args a) {
+  __shared__ unsigned int s_tot[kBins];
+  __shared__ unsigned long long s_keys[kLdsKeys];
+  __shared__ unsigned long long s_prefix, s_k;
+  __shared__ unsigned int s_offs[kListGrid + 1];
+  __shared__ unsigned int s_wave[kFinishThreads / 64];
+  const unsigned int c = int(threadIdx.x) < a.list_grid ? a.count2[threadIdx.x] : 0u;
+  const unsigned int off = block_exclusive_scan<kFinishThreads>(c, s_wave);
+  if (int(threadIdx.x) < a.list_grid) s_offs[threadIdx.x] = off;
+  if (int(threadIdx.x) == a.list_grid - 1) s_offs[a.list_grid] = off + c;
+  if (threadIdx.x == 0) {
+    s_prefix = a.st->prefix1;
+    s_k = a.st->k_rem1;
+  }
+  __syncthreads();
+  const unsigned int total = s_offs[a.list_grid];
+  auto global_entry = [&](unsigned int j) {
+    int lo = 0, hi = a.list_grid - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_offs[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    return a.list2[int64_t(lo) * a.cap2 + (j - s_offs[lo])];
+  };
+  const bool staged = total <= unsigned(kLdsKeys);
+  if (staged) {
+    for (unsigned int j = threadIdx.x; j < total; j += kFinishThreads) s_keys[j] = global_entry(j);
+    __syncthreads();
+  }
+  auto entry = [&](unsigned int j) { return staged ? s_keys[j] : global_entry(j); };
+  for (int pass = 2; pass < 5; ++pass) {
+    for (int b = threadIdx.x; b < kBins; b += kFinishThreads) s_tot[b] = 0u;
+    __syncthreads();
+    const int sh = digit_shift(pass - 1);
+    const unsigned long long want = s_prefix >> sh;
+    for (unsigned int j = threadIdx.x; j < total; j += kFinishThreads) {
+      const unsigned long long key = entry(j);
+      if ((key >> sh) == want) atomicAdd(&s_tot[digit_of(key, pass)], 1u);
+    }
+    __syncthreads();
+    select_digit<kFinishThreads>(s_tot, pass, &s_prefix, &s_k);
+  }
+  const unsigned long long kstar = s_prefix;
+  for (unsigned int j = threadIdx.x; j < total; j += kFinishThreads) {
+    const unsigned long long key = entry(j);
     if (key >= kstar) a.keep[~static_cast<uint32_t>(key)] = 1u;
   }
 }
 
 // The budget alone decides: all = 0 keeps only the current positions, all = 1 keeps everything.
-__global__ __launch_bounds__(kThreads) void fill_kernel(const Args a, int all) {
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < a.n;
-       i += int64_t(gridDim.x) * kThreads) {
+__global__ __launch_bounds__(256) void fill_kernel(const Args a, int all) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < a.n; i += int64_t(gridDim.x) * 256) {
     const int row = row_of(a, i);
     const int t = int(i - int64_t(row) * a.N);
     a.keep[i] = (all != 0 || t == a.current) ? 1u : 0u;
@@ -328,21 +441,26 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(const Args a, int all) {
 }
 
 // kept_per_row[r] = number of ones in row r of the mask.
-__global__ __launch_bounds__(kThreads) void row_count_kernel(const uint8_t* keep, int32_t N,
-                                                             int32_t* out) {
-  __shared__ unsigned int s_wave[kThreads / 64];
+__global__ __launch_bounds__(256) void row_count_kernel(const uint8_t* keep, int32_t N, int32_t* out) {
+  __shared__ unsigned int s_wave[4];
   const uint8_t* row = keep + int64_t(blockIdx.x) * N;
   unsigned int c = 0;
-  for (int t = threadIdx.x; t < N; t += kThreads) c += row[t];
+  for (int t = threadIdx.x; t < N; t += 256) c += row[t];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
   if ((threadIdx.x & 63) == 0) s_wave[threadIdx.x >> 6] = c;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned int total = 0;
-    for (int w = 0; w < kThreads / 64; ++w) total += s_wave[w];
-    out[blockIdx.x] = int32_t(total);
-  }
+  if (threadIdx.x == 0) out[blockIdx.x] = int32_t(s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3]);
+}
+
+Geometry geometry(int64_t n) {
+  Geometry g;
+  const int64_t chunks = (n + kChunk - 1) / kChunk;
+  g.grid = int32_t(chunks < kGrid ? chunks : kGrid);
+  g.cap1 = ((chunks + g.grid - 1) / g.grid) * kChunk;  // entries one workgroup visits, at most
+  g.list_grid = g.grid < kListGrid ? g.grid : kListGrid;
+  g.cap2 = int64_t((g.grid + g.list_grid - 1) / g.list_grid) * g.cap1;
+  return g;
 }
 
 int ceil_log2(int64_t x) {
@@ -386,7 +504,8 @@ extern "C" {
 size_t kv_evict_workspace_size(const kv_evict_params* p) {
   using namespace kvevict;
   if (check(p) != KV_ATTN_OK || !needs_ranking(p)) return 0;
-  return kStateBytes + kHistBytes + size_t(pool_size(p)) * 8u;
+  const Geometry g = geometry(int64_t(p->num_layers) * p->num_heads * p->num_tokens);
+  return kFixedBytes + 8u * size_t(int64_t(g.grid) * g.cap1 + int64_t(g.list_grid) * g.cap2);
 }
 
 kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept_per_row,
@@ -407,7 +526,7 @@ kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept
   if (kvattn::fault_injected("launch")) return KV_ATTN_ERR_HIP;
 
   const int64_t rows = int64_t(p->num_layers) * p->num_heads;
-  Args a;
+  Args a = {};
   a.scores = scores;
   a.keep = keep;
   a.row_stride = p->row_stride;
@@ -420,40 +539,48 @@ kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept
   a.magic_shift = 31 + ceil_log2(p->num_tokens);
   a.magic = ((1ull << a.magic_shift) + uint64_t(p->num_tokens) - 1) / uint64_t(p->num_tokens);
   a.k = rank ? static_cast<unsigned long long>(free_slots(p)) : 0ull;
-  char* ws = static_cast<char*>(workspace);
-  a.st = rank ? reinterpret_cast<State*>(ws) : nullptr;
-  a.hist = rank ? reinterpret_cast<unsigned int*>(ws + kStateBytes) : nullptr;
-  a.list = rank ? reinterpret_cast<unsigned long long*>(ws + kStateBytes + kHistBytes) : nullptr;
+  const Geometry g = geometry(a.n);
+  a.grid = g.grid;
+  a.list_grid = g.list_grid;
+  a.cap1 = g.cap1;
+  a.cap2 = g.cap2;
+  if (rank) {
+    char* ws = static_cast<char*>(workspace);
+    a.st = reinterpret_cast<State*>(ws);
+    a.hist0 = reinterpret_cast<unsigned int*>(ws + kStateBytes);
+    a.hist1 = a.hist0 + size_t(kReplicas0) * kBins;
+    a.count1 = reinterpret_cast<unsigned int*>(ws + kStateBytes + kHistBytes);
+    a.count2 = a.count1 + kGrid;
+    a.list1 = reinterpret_cast<unsigned long long*>(ws + kFixedBytes);
+    a.list2 = a.list1 + int64_t(g.grid) * g.cap1;
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t chunks = (a.n + kChunk - 1) / kChunk;
-  const uint32_t grid = uint32_t(chunks < kMaxGrid ? chunks : kMaxGrid);
   if (!rank) {
     const int all = free_slots(p) > 0 ? 1 : 0;  // K >= pool: everything stays
-    const int64_t blocks = (a.n + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(fill_kernel, dim3(uint32_t(blocks < kMaxGrid ? blocks : kMaxGrid)),
-                       dim3(kThreads), 0, s, a, all);
+    const int64_t blocks = (a.n + 255) / 256;
+    hipLaunchKernelGGL(fill_kernel, dim3(uint32_t(blocks < 2048 ? blocks : 2048)), dim3(256), 0, s,
+                       a, all);
     if (hipGetLastError() != hipSuccess) return KV_ATTN_ERR_HIP;
   } else {
     const bool vec = p->num_tokens % 4 == 0 && p->row_stride % 4 == 0 && aligned(scores, 16) &&
                      aligned(keep, 4);
-    hipLaunchKernelGGL(init_kernel, dim3((kPasses * kBins + kThreads - 1) / kThreads),
-                       dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(init_kernel, dim3(((kReplicas0 + kReplicas1) * kBins / 4 + 255) / 256),
+                       dim3(256), 0, s, a);
     if (vec) {
-      hipLaunchKernelGGL(pass0_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
-      hipLaunchKernelGGL(pass1_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL(pass0_kernel<true>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
+      hipLaunchKernelGGL(pass1_kernel<true>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
     } else {
-      hipLaunchKernelGGL(pass0_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
-      hipLaunchKernelGGL(pass1_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL(pass0_kernel<false>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
+      hipLaunchKernelGGL(pass1_kernel<false>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
     }
-    for (int pass = 2; pass < kPasses; ++pass)
-      hipLaunchKernelGGL(list_pass_kernel, dim3(kListGrid), dim3(kThreads), 0, s, a, pass);
-    hipLaunchKernelGGL(patch_kernel, dim3(kListGrid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(list_kernel, dim3(g.list_grid), dim3(kFinishThreads), 0, s, a);
+    hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kFinishThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return KV_ATTN_ERR_HIP;
   }
   if (kept_per_row != nullptr) {
-    hipLaunchKernelGGL(row_count_kernel, dim3(uint32_t(rows)), dim3(kThreads), 0, s, keep,
-                       p->num_tokens, kept_per_row);
+    hipLaunchKernelGGL(row_count_kernel, dim3(uint32_t(rows)), dim3(256), 0, s, keep, p->num_tokens,
+                       kept_per_row);
     if (hipGetLastError() != hipSuccess) return KV_ATTN_ERR_HIP;
   }
   return KV_ATTN_OK;

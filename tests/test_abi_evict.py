@@ -47,12 +47,14 @@ def test_params_layout_matches_the_header():
 
 
 def test_workspace_size_follows_the_budget():
-    L, H, N = 2, 3, 10
-    pool = L * H * (N - 1)
-    fixed = 256 + 5 * 8192 * 4
-    for M, want in [(0, 0), (L * H, 0), (L * H + 1, fixed + 8 * pool),
-                    (L * H + pool - 1, fixed + 8 * pool), (L * H + pool, 0), (10**12, 0)]:
-        assert E.kv_evict_workspace_size(E.make_evict_params(L, H, N, M)) == want, M
+    fixed = 397568
+    for L, H, N in [(2, 3, 10), (32, 32, 4096), (32, 8, 131072), (3, 5, 777)]:
+        n, pool = L * H * N, L * H * (N - 1)
+        for M in (0, L * H, L * H + pool, 10**12):  # the budget alone decides
+            assert E.kv_evict_workspace_size(E.make_evict_params(L, H, N, M)) == 0, M
+        for M in (L * H + 1, L * H + pool // 2, L * H + pool - 1):
+            ws = E.kv_evict_workspace_size(E.make_evict_params(L, H, N, M))
+            assert fixed + 16 * n <= ws <= fixed + 32 * (n + 256 * 16384), (L, H, N, M, ws)
     assert E.kv_evict_workspace_size(E.make_evict_params(1, 1, 1, 5)) == 0  # N = 1: no pool
 
 
