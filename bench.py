@@ -416,6 +416,13 @@ def bench_evict(args, W):
     e1.record()
     torch.cuda.synchronize()
     us = 1e3 * e0.elapsed_time(e1) / args.steps
+    if args.calib_copy_mib:  # plain copies of known size, for the counter-calibration runs
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     kept = int(keep.sum().item())
     alg_bytes = 5 * n
     achieved = alg_bytes / (us * 1e-6) / 1e9

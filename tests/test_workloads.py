@@ -165,3 +165,53 @@ def test_window_poisons_exactly_the_unattended_positions(paged, layout):
     got = decode_attention(b["q"], b["k_cache"], b["v_cache"], b["ctx_lens"], b["block_table"],
                            block_size=bs, window=40, num_sinks=3)
     assert np.isfinite(got).all() and np.array_equal(ref, got)
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_gamma_tokens_spare_the_union_of_their_windows(paged):
+    """With gamma query tokens, q is [B, gamma, h_q, d] and the window poisoning spares every
+    position some token attends (the union of the tokens' windows and the sinks)."""
+    from oracle import attended_positions, verify_attention
+    ctx, gamma, window, sinks = (200, 37, 3), 4, 30, 2
+    kw = dict(batch=3, ctx=ctx, paged=paged, num_sinks=sinks, capacity=None if paged else 210)
+    plain = W.make_workload(W.preset("C5", num_queries=gamma, **kw))
+    win = W.make_workload(W.preset("C5", num_queries=gamma, window=window, **kw))
+    assert tuple(win.q.shape) == (3, gamma, 64, 128)
+    assert torch.equal(plain.q.view(torch.int16), win.q.view(torch.int16))
+    a, b = W.oracle_view(plain), W.oracle_view(win)
+    isnan = lambda u: (u & 0x7FFF) > 0x7F80  # noqa: E731
+    for s, length in enumerate(ctx):
+        keep = set()
+        for j in range(gamma):
+            visible = length - gamma + 1 + j
+            if visible > 0:
+                keep |= set(attended_positions(visible, window, sinks).tolist())
+        for t in range(length):
+            blk, slot = ((a["block_table"][s, t // 16], t % 16) if paged else (s, t))
+            y = b["k_cache"][blk, slot]
+            assert (not isnan(y).any()) if t in keep else isnan(y).all(), (s, t)
+    bs = a["block_size"] if paged else None
+    ref = verify_attention(a["q"], a["k_cache"], a["v_cache"], a["ctx_lens"], a["block_table"],
+                           block_size=bs, window=window, num_sinks=sinks)
+    got = verify_attention(b["q"], b["k_cache"], b["v_cache"], b["ctx_lens"], b["block_table"],
+                           block_size=bs, window=window, num_sinks=sinks)
+    assert np.isfinite(got).all() and np.array_equal(ref, got)
+
+
+@pytest.mark.parametrize("kind", ["lognormal", "normal", "levels", "equal"])
+def test_scores_are_seeded_and_strided_views_hide_their_padding(kind):
+    a = W.make_scores(3, 4, 50, kind, seed=5)
+    b = W.make_scores(3, 4, 50, kind, seed=5)
+    assert a.shape == (3, 4, 50) and a.dtype == torch.float32 and a.is_contiguous()
+    assert torch.equal(a, b)
+    s = W.make_scores(3, 4, 50, kind, seed=5, row_stride=53)
+    assert s.shape == (3, 4, 50) and s.stride() == (4 * 53, 53, 1)
+    assert torch.isfinite(s).all()
+    store = s.as_strided((12, 53), (53, 1))
+    assert torch.isnan(store[:, 50:]).all()   # the padding is never meant to be read
+    if kind == "lognormal":
+        assert (a > 0).all()
+    if kind == "levels":
+        assert set(a.unique().tolist()) <= {0.0, 0.25, 0.5, 1.0}
+    if kind == "equal":
+        assert (a == 1.0).all()
