@@ -22,6 +22,9 @@ kv_append
 verify_attention
     γ new query tokens per sequence attending causally among themselves (the target model's
     check of a speculative-decoding draft).
+position_scores
+    The attention weight each cached position receives in a decode step, summed over the query
+    heads of its KV head (the per-entry score eviction ranks by).
 evict_select
     Budgeted KV eviction selection: the current position of every (layer, head) kept, the rest
     ranked in one global pool by (−score, layer, head, token) and the first M − L·H kept.
@@ -51,3 +54,4 @@ from .fsum_reference import decode_attention_fsum  # noqa: F401
 from .kv_append import append_kv  # noqa: F401
 from .verify_attention import verify_attention  # noqa: F401
 from .evict_select import evict_select  # noqa: F401
+from .position_scores import position_scores  # noqa: F401
