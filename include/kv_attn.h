@@ -266,6 +266,34 @@ kv_attn_status kv_attn_append_decode(const void* q, const void* k_new, const voi
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode with score export: kv_attn_decode, and in addition the attention weight every cached
+ * position received, summed over the g query heads that share its KV head — the per-entry score
+ * that eviction policies rank by (Ch. 19 §19.4.3: a few "heavy hitter" tokens collect most of
+ * the attention; the eviction exercise takes one score per (layer, head, token)).
+ *
+ * token_scores : device fp32 [batch, num_kv_heads, max_ctx_len] contiguous. For every attended
+ *                position t of sequence b (t < ctx_lens[b], and inside the window when one is
+ *                set) entry (b, kvh, t) = sum over j < g of softmax weight of t for query head
+ *                kvh*g + j; the weights of one query head sum to 1, so a sequence's entries per
+ *                KV head sum to g. accumulate == 0 writes every entry (unattended ones 0);
+ *                accumulate != 0 adds the weights to the attended entries and leaves the others
+ *                (a running sum across decode steps, as H2O keeps). Must not alias any input.
+ * workspace    : at least kv_attn_scores_workspace_size(p) bytes, 16-byte aligned, always
+ *                required (the kernels keep the base-2 scores of every visited position and
+ *                the final (m, l) of every query row there: the decode workspace, then
+ *                4 * batch * num_q_heads * roundup(max_ctx_len, 16) + 8 * batch * num_q_heads
+ *                bytes).
+ * One query token per sequence, and q and KV both bf16 or both fp32 (otherwise
+ * KV_ATTN_ERR_UNSUPPORTED). Other arguments, checks and errors as for kv_attn_decode.
+ */
+size_t kv_attn_scores_workspace_size(const kv_attn_params* p);
+kv_attn_status kv_attn_decode_scores(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                                     float* token_scores, int32_t accumulate,
+                                     const kv_attn_params* p, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Host-side check of the device-resident inputs' contents (debug aid; runs on the CPU and
  * touches no device): every 0 <= ctx_lens[b] <= max_ctx_len and, for a paged cache
  * (block_table != NULL), every entry 0 <= block_table[b][i] < num_blocks for

@@ -141,10 +141,30 @@ AppendArgs append_args(const kv_attn_params* p, const void* k_new, const void* v
 
 // Shared body of kv_attn_decode / _split / _merge: validation, planning, then the passes in
 // `passes`. Every host-side check runs before the first HIP call.
+// Score export (token_scores != nullptr): where the logits and row statistics go in the workspace.
+struct ScoreLayout {
+  uint64_t logits_offset, stats_offset, total;
+  int64_t ld;
+};
+
+uint64_t round256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+ScoreLayout score_layout(const kv_attn_params* p, const Plan& plan) {
+  ScoreLayout l;
+  const int64_t rows = int64_t(p->batch) * p->num_q_heads;
+  const int64_t ctx = p->max_ctx_len > 0 ? p->max_ctx_len : 1;
+  l.ld = (ctx + kTile - 1) / kTile * kTile;
+  l.logits_offset = round256(plan.workspace_bytes);
+  l.stats_offset = l.logits_offset + round256(uint64_t(rows) * uint64_t(l.ld) * 4u);
+  l.total = l.stats_offset + uint64_t(rows) * 8u;
+  return l;
+}
+
 kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* ctx_lens, float* out,
                            const kv_attn_params* p, void* workspace, size_t workspace_bytes,
-                           void* stream, const void* k_new = nullptr, const void* v_new = nullptr) {
+                           void* stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                           float* token_scores = nullptr, int32_t accumulate = 0) {
   if (p == nullptr || ctx_lens == nullptr || out == nullptr) return KV_ATTN_ERR_NULL;
   if ((passes & kPassSplit) && (q == nullptr || k_cache == nullptr || v_cache == nullptr))
     return KV_ATTN_ERR_NULL;
@@ -163,7 +183,19 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
   Plan plan;
   st = make_plan(p, cus, &plan);
   if (st != KV_ATTN_OK) return st;
-  if (plan.num_splits > 1) {
+  const bool scores = token_scores != nullptr;
+  ScoreLayout sl = {};
+  if (scores) {
+    if (plan.num_queries > 1) return KV_ATTN_ERR_UNSUPPORTED;  // one query token per sequence
+    // Score export is compiled for bf16 q and KV (matrix cores) and for fp32 q and KV.
+    const bool bf16_pair = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && plan.variant == 1;
+    const bool f32_pair = p->q_dtype == KV_ATTN_F32 && p->kv_dtype == KV_ATTN_F32;
+    if (!bf16_pair && !f32_pair) return KV_ATTN_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(token_scores) & 3u) != 0) return KV_ATTN_ERR_UNSUPPORTED;
+    sl = score_layout(p, plan);
+    if (workspace == nullptr || workspace_bytes < sl.total) return KV_ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KV_ATTN_ERR_UNSUPPORTED;
+  } else if (plan.num_splits > 1) {
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return KV_ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KV_ATTN_ERR_UNSUPPORTED;
   }
@@ -174,6 +206,10 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     st = debug_validate(block_table, ctx_lens, p, s);
     if (st != KV_ATTN_OK) return st;
   }
+  float* logits = scores ? reinterpret_cast<float*>(static_cast<char*>(workspace) + sl.logits_offset)
+                        : nullptr;
+  float* row_stats = scores ? reinterpret_cast<float*>(static_cast<char*>(workspace) + sl.stats_offset)
+                            : nullptr;
   float* o_part = plan.num_splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
   float* ml_part = plan.num_splits > 1
                        ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.o_part_bytes)
@@ -213,6 +249,9 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.window = p->window;
     a.num_sinks = p->num_sinks;
     a.num_queries = plan.num_queries;
+    a.logits = logits;
+    a.logits_ld = sl.ld;
+    a.row_stats = plan.num_splits == 1 ? row_stats : nullptr;
     const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
     a.scale_log2 = float(scale * 1.4426950408889634);  // log2(e)
     if (launch_split(a, plan, p->head_dim, paged, p->q_dtype == KV_ATTN_BF16,
@@ -234,7 +273,25 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     m.window = p->window;
     m.num_sinks = p->num_sinks;
     m.num_queries = plan.num_queries;
+    m.row_stats = row_stats;
     if (launch_merge(m, p->head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
+  }
+  if (scores && (passes & kPassMerge)) {
+    ScoreArgs sa;
+    sa.logits = logits;
+    sa.row_stats = row_stats;
+    sa.ctx_lens = ctx_lens;
+    sa.scores = token_scores;
+    sa.logits_ld = sl.ld;
+    sa.scores_ld = p->max_ctx_len;
+    sa.h_kv = p->num_kv_heads;
+    sa.group = p->num_q_heads / p->num_kv_heads;
+    sa.max_ctx = p->max_ctx_len;
+    sa.window = p->window;
+    sa.num_sinks = p->num_sinks;
+    sa.accumulate = accumulate;
+    sa.chunks = int32_t((int64_t(p->max_ctx_len) + kScoreChunk - 1) / kScoreChunk);
+    if (launch_scores(sa, int64_t(p->batch) * p->num_kv_heads, stream) != 0) return KV_ATTN_ERR_HIP;
   }
   if (debug_mode()) {
     if (hipStreamSynchronize(s) != hipSuccess || hipGetLastError() != hipSuccess) return KV_ATTN_ERR_HIP;
@@ -301,6 +358,26 @@ kv_attn_status kv_attn_append_decode(const void* q, const void* k_new, const voi
                              workspace_bytes, stream, k_new, v_new);
 }
 
+size_t kv_attn_scores_workspace_size(const kv_attn_params* p) {
+  if (p == nullptr || kvattn::validate_params(p) != KV_ATTN_OK) return 0;
+  const int cus = kvattn::current_cu_count();
+  if (cus <= 0) return 0;
+  kvattn::Plan plan;
+  if (kvattn::make_plan(p, cus, &plan) != KV_ATTN_OK || plan.num_queries > 1) return 0;
+  return size_t(kvattn::score_layout(p, plan).total);
+}
+
+kv_attn_status kv_attn_decode_scores(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* ctx_lens, float* out,
+                                     float* token_scores, int32_t accumulate,
+                                     const kv_attn_params* p, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (token_scores == nullptr) return KV_ATTN_ERR_NULL;
+  return kvattn::decode_impl(kvattn::kPassSplit | kvattn::kPassMerge, q, k_cache, v_cache,
+                             block_table, ctx_lens, out, p, workspace, workspace_bytes, stream,
+                             nullptr, nullptr, token_scores, accumulate);
+}
+
 kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
                              const int32_t* num_valid, float* out, int32_t rows,
                              int32_t num_splits, int32_t head_dim, void* stream) {
@@ -323,6 +400,7 @@ kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,
   m.window = 0;
   m.num_sinks = 0;
   m.num_queries = 1;
+  m.row_stats = nullptr;
   if (kvattn::launch_merge(m, head_dim, stream) != 0) return KV_ATTN_ERR_HIP;
   if (kvattn::debug_mode()) {
     if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess ||

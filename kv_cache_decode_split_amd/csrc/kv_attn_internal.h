@@ -50,6 +50,10 @@ struct SplitArgs {
   int32_t window;              // > 0: attend only the last `window` positions plus the sinks
   int32_t num_sinks;           // leading positions always attended when a window is set
   int32_t num_queries;         // query tokens per sequence (rows mode; 1 otherwise)
+  float* logits;               // nullptr, or [B * h_q, logits_ld]: base-2 scores of every visited
+                               // position (one query token per sequence only)
+  int64_t logits_ld;           // multiple of kTile, >= max_ctx rounded up to kTile
+  float* row_stats;            // nullptr, or [B * h_q, 2]: final (m, l) per row (num_splits == 1)
 };
 
 struct MergeArgs {
@@ -66,7 +70,27 @@ struct MergeArgs {
   int32_t window;              // decode path: as in SplitArgs
   int32_t num_sinks;
   int32_t num_queries;
+  float* row_stats;            // nullptr, or [rows, 2]: the merged (m, l) of every row
 };
+
+// Per-position attention weights: for every (sequence, KV head, position) the sum over the
+// group's query heads of 2^(s - m) / l, from the logits and row statistics the decode wrote.
+struct ScoreArgs {
+  const float* logits;         // [B * h_q, logits_ld]
+  const float* row_stats;      // [B * h_q, 2]
+  const int32_t* ctx_lens;
+  float* scores;               // [B, h_kv, scores_ld]
+  int64_t logits_ld;
+  int64_t scores_ld;           // = max_ctx
+  int32_t h_kv;
+  int32_t group;
+  int32_t max_ctx;
+  int32_t window;
+  int32_t num_sinks;
+  int32_t accumulate;          // 0: write every entry (unattended ones 0); else add to attended ones
+  int32_t chunks;              // position chunks of kScoreChunk per (sequence, KV head)
+};
+constexpr int kScoreChunk = 1024;
 
 // Everything the append kernel needs: one new K/V row per (sequence, KV head) is stored at
 // logical position positions[b] + pos_offset of sequence b.
@@ -116,6 +140,7 @@ int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged,
                  bool kv_bf16, void* stream);
 int launch_merge(const MergeArgs& a, int head_dim, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
+int launch_scores(const ScoreArgs& a, int64_t units, void* stream);
 
 }  // namespace kvattn
 

@@ -173,11 +173,15 @@ __device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
 #define KV_ATTN_WAVES_PER_EU 0
 #endif
 
-// PAGED: 0 contiguous, 1 paged, 2 decided at run time (vector variant only).
+// PAGED: 0 contiguous, 1 paged, 2 decided at run time.
 // R = 0: one query token per sequence (G = compiled group width). R > 0 ("rows" mode, variant 2):
 // num_queries tokens per sequence, the group's query rows (token-major, then head) packed into R
 // blocks of 16 MFMA columns; scores and P.V both on the matrix cores (G unused).
-template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED, int R = 0>
+// SCORES: score export (one query token): every visited position's base-2 score goes to
+// a.logits and, with one split, each row's final (m, l) to a.row_stats. A separate
+// instantiation, so that the kernels without it keep their register allocation.
+template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED, int R = 0,
+          bool SCORES = false>
 __global__ __launch_bounds__(kSplitThreads)
 #if KV_ATTN_WAVES_PER_EU > 0
 __attribute__((amdgpu_waves_per_eu(MFMA && G <= 8 ? KV_ATTN_WAVES_PER_EU : 1)))
@@ -186,6 +190,7 @@ void split_kernel(const SplitArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(!MFMA || (Q_BF16 && KV_BF16), "matrix-core scores need bf16 q and KV");
   static_assert(R == 0 || MFMA, "rows mode runs on the matrix cores");
+  static_assert(!(SCORES && R > 0), "score export takes one query token per sequence");
   constexpr bool ROWS = R > 0;
   constexpr int NR = ROWS ? 16 * R : G;       // query rows held per (sequence, KV head)
   constexpr int EPL = D / 16;                 // elements per lane of a 16-lane row
@@ -243,6 +248,10 @@ void split_kernel(const SplitArgs a) {
     if (S == 1) {
       for (int idx = threadIdx.x; idx < rows * D; idx += kSplitThreads)
         a.out[out_row(idx / D) * D + idx % D] = 0.f;
+      if (SCORES && a.row_stats != nullptr && threadIdx.x < rows) {
+        a.row_stats[out_row(threadIdx.x) * 2 + 0] = neg_inf();
+        a.row_stats[out_row(threadIdx.x) * 2 + 1] = 0.f;
+      }
     }
     return;
   }
@@ -421,6 +430,9 @@ void split_kernel(const SplitArgs a) {
       float s[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[r] = attended(4 * q4 + r) ? acc[r] * a.scale_log2 : neg_inf();
+      if (SCORES && r16 < g)  // score export: positions p0 + 4*q4 .. +3 of head r16
+        *reinterpret_cast<f32x4_t*>(a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * g + r16) * a.logits_ld +
+                                    p0 + 4 * q4) = f32x4_t{s[0], s[1], s[2], s[3]};
       float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mt = max_xor32(max_xor16(mt));
       const float m_new = fmaxf(m_run, mt);
@@ -452,6 +464,13 @@ void split_kernel(const SplitArgs a) {
           x = row_sum16(x);
           s[i][j] = valid ? x * a.scale_log2 : neg_inf();
         }
+      }
+      if constexpr (SCORES) {  // score export: lane r16 = j writes head j's four positions
+        static_for<0, G>([&](auto J) __attribute__((always_inline)) {
+          if (J() < g && r16 == J())
+            *reinterpret_cast<f32x4_t*>(a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * g + J()) * a.logits_ld +
+                                        p0 + 4 * q4) = f32x4_t{s[0][J()], s[1][J()], s[2][J()], s[3][J()]};
+        });
       }
       bool any_change = false;
       float cv[G];
@@ -678,6 +697,10 @@ void split_kernel(const SplitArgs a) {
     const int64_t row = out_row(j);
     if (S == 1) {
       a.out[row * D + e] = L > 0.f ? acc / L : 0.f;  // L = 0: a query token that sees nothing
+      if (SCORES && a.row_stats != nullptr && e == 0) {
+        a.row_stats[row * 2 + 0] = M;
+        a.row_stats[row * 2 + 1] = L;
+      }
     } else {
       const int64_t slot = row * S + split;
       a.o_part[slot * D + e] = acc;
@@ -785,6 +808,49 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
     for (int k = 1; k < SUB; ++k) total += s_acc[k][tid];
     a.out[int64_t(row) * D + tid] = L > 0.f ? total / L : 0.f;
   }
+  if (a.row_stats != nullptr && tid == 0) {
+    a.row_stats[int64_t(row) * 2 + 0] = M;
+    a.row_stats[int64_t(row) * 2 + 1] = L;
+  }
+}
+
+// Per-position attention weights (score export): one workgroup per (sequence, KV head, chunk of
+// kScoreChunk positions). The weight of an attended position t for query row j is
+// 2^(s_jt - m_j) / l_j with the row's final base-2 maximum m_j and sum l_j; the group's rows are
+// summed. Unattended positions (past the length, or outside the window) get 0, or are left
+// alone when accumulating.
+__global__ __launch_bounds__(256) void score_kernel(const ScoreArgs a) {
+  __shared__ float s_m[16], s_rl[16];
+  const int unit = int(blockIdx.x) / a.chunks;  // b * h_kv + kvh
+  const int chunk = int(blockIdx.x) - unit * a.chunks;
+  const int b = unit / a.h_kv;
+  const int64_t row0 = int64_t(unit) * a.group;  // first query row of the KV head
+  if (int(threadIdx.x) < a.group) {
+    const float l = a.row_stats[(row0 + threadIdx.x) * 2 + 1];
+    s_m[threadIdx.x] = a.row_stats[(row0 + threadIdx.x) * 2 + 0];
+    s_rl[threadIdx.x] = l > 0.f ? 1.f / l : 0.f;
+  }
+  __syncthreads();
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  int sink_end = 0, win_start = 0;
+  if (a.window > 0) {
+    sink_end = min(a.num_sinks, ctx);
+    win_start = max(ctx - a.window, 0);
+  }
+  float* dst = a.scores + int64_t(unit) * a.scores_ld;
+  const int end = int(min(int64_t(chunk + 1) * kScoreChunk, a.scores_ld));
+  for (int t = chunk * kScoreChunk + int(threadIdx.x); t < end; t += 256) {
+    const bool attended = t < ctx && (t < sink_end || t >= win_start);
+    if (!attended) {
+      if (a.accumulate == 0) dst[t] = 0.f;
+      continue;
+    }
+    float w = 0.f;
+    for (int j = 0; j < a.group; ++j)
+      w = fmaf(exp2_fast(a.logits[(row0 + j) * a.logits_ld + t] - s_m[j]), s_rl[j], w);
+    dst[t] = a.accumulate != 0 ? dst[t] + w : w;
+  }
 }
 
 // Append: one thread per 16-byte piece of a new K (and V) row. The destination follows the
@@ -820,11 +886,21 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(a.v) + vdst) = vx;
 }
 
-template <int D, int G, bool QB, bool KB, bool MF, int PG, int R = 0>
+template <int D, int G, bool QB, bool KB, bool MF, int PG, int R = 0, bool SC = false>
 int launch_one(const SplitArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG, R>), dim3(uint32_t(grid)),
+  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG, R, SC>), dim3(uint32_t(grid)),
                      dim3(kSplitThreads), 0, stream, a);
   return int(hipGetLastError());
+}
+
+// Score export: bf16 q and KV on the matrix cores, or fp32 q and KV on the vector path; the
+// cache layout is decided at run time.
+template <int D, int G>
+int launch_scores_variant(const SplitArgs& a, const Plan& plan, bool q_bf16, bool kv_bf16,
+                          hipStream_t s) {
+  if (plan.variant == 1) return launch_one<D, G, true, true, true, 2, 0, true>(a, plan.grid_split, s);
+  if (!q_bf16 && !kv_bf16) return launch_one<D, G, false, false, false, 2, 0, true>(a, plan.grid_split, s);
+  return int(hipErrorInvalidValue);
 }
 
 // Rows mode (several query tokens per sequence): bf16 only, 1 or 2 blocks of 16 query rows.
@@ -842,6 +918,7 @@ int launch_rows(const SplitArgs& a, const Plan& plan, bool paged, hipStream_t s)
 template <int D, int G>
 int launch_dtype(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16, bool kv_bf16,
                  hipStream_t s) {
+  if (a.logits != nullptr) return launch_scores_variant<D, G>(a, plan, q_bf16, kv_bf16, s);
   if (plan.variant == 1) {
     return paged ? launch_one<D, G, true, true, true, 1>(a, plan.grid_split, s)
                  : launch_one<D, G, true, true, true, 0>(a, plan.grid_split, s);
@@ -885,6 +962,14 @@ int launch_append(const AppendArgs& a, void* stream) {
   if (a.total <= 0) return 0;
   const uint32_t grid = uint32_t((int64_t(a.total) + 255) / 256);
   hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(256), 0, s, a);
+  return int(hipGetLastError());
+}
+
+int launch_scores(const ScoreArgs& a, int64_t units, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t grid = units * a.chunks;
+  if (grid <= 0) return 0;
+  hipLaunchKernelGGL(score_kernel, dim3(uint32_t(grid)), dim3(256), 0, s, a);
   return int(hipGetLastError());
 }
 

@@ -36,6 +36,8 @@ __all__ = [
     "decode_call_for",
     "kv_attn_merge",
     "kv_attn_validate_host",
+    "kv_attn_scores_workspace_size",
+    "kv_attn_decode_scores",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -67,6 +69,8 @@ EXPORTED_SYMBOLS = (
     "kv_attn_append_decode",
     "kv_attn_merge",
     "kv_attn_validate_host",
+    "kv_attn_scores_workspace_size",
+    "kv_attn_decode_scores",
 )
 
 
@@ -146,6 +150,11 @@ def _load():
     lib.kv_attn_merge.restype = ctypes.c_int
     lib.kv_attn_validate_host.argtypes = [vp, vp, P(kv_attn_params)]
     lib.kv_attn_validate_host.restype = ctypes.c_int
+    lib.kv_attn_scores_workspace_size.argtypes = [P(kv_attn_params)]
+    lib.kv_attn_scores_workspace_size.restype = ctypes.c_size_t
+    lib.kv_attn_decode_scores.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                          P(kv_attn_params), vp, ctypes.c_size_t, vp]
+    lib.kv_attn_decode_scores.restype = ctypes.c_int
     return lib
 
 
@@ -246,7 +255,7 @@ class DecodeCall:
                  k_strides: Sequence[int], v_strides: Sequence[int], block_size: int,
                  num_blocks: int, max_ctx_len: Optional[int] = None, scale: float = 0.0,
                  num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
-                 window: Optional[int] = None, num_sinks: int = 0):
+                 window: Optional[int] = None, num_sinks: int = 0, with_scores: bool = False):
         if q.dim() not in (3, 4) or not q.is_contiguous():
             raise ValueError("q must be a contiguous [B, h_q, d] or [B, gamma, h_q, d] tensor")
         B, hq, d = q.shape[0], q.shape[-2], q.shape[-1]
@@ -282,7 +291,10 @@ class DecodeCall:
             window=window, num_sinks=num_sinks, num_queries=nq)
         _check_extent(k_cache, k_strides, num_blocks, block_size, hkv, d, "k_cache")
         _check_extent(v_cache, v_strides, num_blocks, block_size, hkv, d, "v_cache")
-        ws_bytes = kv_attn_workspace_size(self.params)
+        ws_bytes = (kv_attn_scores_workspace_size(self.params) if with_scores
+                    else kv_attn_workspace_size(self.params))
+        if with_scores and ws_bytes == 0:
+            raise KvAttnError(KV_ATTN_ERR_UNSUPPORTED, "kv_attn_scores_workspace_size")
         if ws_bytes and workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         if workspace is not None and workspace.device != dev:
@@ -303,6 +315,21 @@ class DecodeCall:
                                  _stream_handle(stream))
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode")
+
+    def decode_scores(self, token_scores: torch.Tensor, accumulate: bool = False,
+                      stream=None) -> None:
+        """Decode and write (or, with ``accumulate``, add) each attended position's attention
+        weight summed over its KV head's query heads into ``token_scores``, a contiguous fp32
+        [B, h_kv, max_ctx_len] tensor (build the call with ``with_scores=True``)."""
+        p = self.params
+        want = (p.batch, p.num_kv_heads, p.max_ctx_len)
+        if (tuple(token_scores.shape) != want or token_scores.dtype != torch.float32
+                or not token_scores.is_contiguous() or token_scores.device != self._keep[0].device):
+            raise ValueError(f"token_scores must be a contiguous fp32 {list(want)} tensor on q's device")
+        st = _lib.kv_attn_decode_scores(*self._ptrs, token_scores.data_ptr(), int(bool(accumulate)),
+                                        ctypes.byref(self.params), *self._ws, _stream_handle(stream))
+        if st != KV_ATTN_OK:
+            raise KvAttnError(st, "kv_attn_decode_scores")
 
     def split(self, stream=None) -> None:
         st = _lib.kv_attn_decode_split(*self._ptrs, ctypes.byref(self.params), *self._ws,
@@ -341,6 +368,17 @@ def _check_new_rows(k_new, v_new, cache, batch, num_kv_heads, head_dim, rows=1):
 def kv_attn_decode(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None, **kwargs) -> None:
     """Enqueue one decode-attention step (both passes); arguments as for :class:`DecodeCall`."""
     DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, **kwargs).decode(stream)
+
+
+def kv_attn_scores_workspace_size(params: kv_attn_params) -> int:
+    return int(_lib.kv_attn_scores_workspace_size(ctypes.byref(params)))
+
+
+def kv_attn_decode_scores(q, k_cache, v_cache, block_table, ctx_lens, out, token_scores, *,
+                          accumulate: bool = False, stream=None, **kwargs) -> None:
+    """Decode plus per-position attention weights (see :meth:`DecodeCall.decode_scores`)."""
+    DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, with_scores=True,
+               **kwargs).decode_scores(token_scores, accumulate, stream)
 
 
 def kv_attn_decode_split(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None,
