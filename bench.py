@@ -21,6 +21,9 @@ with events, never time host submission):
     that duration (the merge launches follow outside the events);
   * with --window W, only the attended positions (the first sinks and the last W) count as
     bytes, both in value and in roofline.achieved;
+  * with --scores every layer also exports the per-position attention weights (the split
+    kernel's score-export instantiation, then the weighting kernel) in pass A; pass B still
+    times the regular split kernel;
   * with --gamma G (speculative-decoding verification) every sequence has G query tokens, the
     last G cached positions, each attending to its own prefix; bytes count the union of the
     positions they attend (each KV element once) and tokens_per_s counts B * G tokens;
@@ -92,6 +95,9 @@ def parse_args():
     ap.add_argument("--gamma", type=int, default=1,
                     help="query tokens per sequence (speculative-decoding verification: the last "
                          "gamma cached positions, causal among themselves)")
+    ap.add_argument("--scores", action="store_true",
+                    help="each layer also exports the attention weight of every cached position "
+                         "(kv_attn_decode_scores)")
     ap.add_argument("--evict", choices=["E1", "E2"], default=None,
                     help="time the budgeted eviction selection on this score workload instead of "
                          "decode attention")
@@ -151,7 +157,13 @@ def main():
     outs = [torch.empty(w.q.shape, dtype=torch.float32, device="cuda") for w in wls]
     # One call (and workspace) per layer, so that pass B can run all split launches before the
     # merges without one layer's split states overwriting another's.
-    calls = [K.decode_call_for(w, o, num_splits=args.num_splits) for w, o in zip(wls, outs)]
+    if args.scores and (args.append or args.gamma > 1):
+        print("bench.py: --scores takes one query token and no --append", file=sys.stderr)
+        sys.exit(2)
+    calls = [K.decode_call_for(w, o, num_splits=args.num_splits, with_scores=args.scores)
+             for w, o in zip(wls, outs)]
+    score_bufs = ([torch.empty((spec.batch, spec.num_kv_heads, w.max_ctx_len), dtype=torch.float32,
+                               device="cuda") for w in wls] if args.scores else [])
     plan = calls[0].plan()
     elem = 2 if spec.kv_dtype == "bf16" else 4
     lens = [int(x) for x in wls[0].ctx_lens.cpu().tolist()]
@@ -179,6 +191,10 @@ def main():
                               for _ in range(2)))
 
     def step():
+        if args.scores:
+            for c, buf in zip(calls, score_bufs):
+                c.decode_scores(buf)
+            return
         if args.append:
             for c, (kn, vn) in zip(calls, news):
                 c.append_decode(kn, vn)
@@ -358,6 +374,9 @@ def main():
         "outputs_finite": finite,
         "cpu_baseline": cpu,
     }
+    if args.scores:
+        line["config"]["scores"] = ("each layer also writes every attended position's attention "
+                                    "weight summed over its KV head's query heads")
     if args.append:
         line["config"]["append"] = ("each layer appends the current token's K/V before attending"
                                     if gamma == 1 else

@@ -193,6 +193,8 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     if (!bf16_pair && !f32_pair) return KV_ATTN_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(token_scores) & 3u) != 0) return KV_ATTN_ERR_UNSUPPORTED;
     sl = score_layout(p, plan);
+    // One (sequence, KV head)'s scores are addressed by a 31-bit byte offset.
+    if (sl.ld * (p->num_q_heads / p->num_kv_heads) * 4 >= (int64_t(1) << 31)) return KV_ATTN_ERR_UNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < sl.total) return KV_ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KV_ATTN_ERR_UNSUPPORTED;
   } else if (plan.num_splits > 1) {

@@ -55,6 +55,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define KV_ATTN_NONTEMPORAL 1
 #endif
 constexpr int kDepth = KV_ATTN_DEPTH;  // tiles in flight per wave
+constexpr int kBufferRsrcWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -414,6 +415,21 @@ void split_kernel(const SplitArgs a) {
     for (int i = 0; i < 4; ++i) f.vr[i] = load_seg<SEG>(vt + o.v[i]);
   };
 
+  // Score export: the scores of positions pos .. pos+3 for query head j of this (sequence, KV
+  // head) go to row b*h_q + kvh*g + j of a.logits ([B*h_q, logits_ld]). Every lane issues one
+  // bounds-checked 16-byte buffer store, padding heads (j >= g) with an offset past the end that
+  // the hardware drops: a branch around the stores would hide them from the wait counts on the
+  // path that skips them, and the loads of the next tiles would then be waited for too early on
+  // the path that takes them. (a.logits is null outside the score-export instantiations; the
+  // descriptor is then unused.)
+  const __amdgpu_buffer_rsrc_t score_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      SCORES ? a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * g) * a.logits_ld : a.logits, 0,
+      SCORES ? int(a.logits_ld * g * 4) : 0, kBufferRsrcWord3);
+  auto store_scores = [&](f32x4_t v, int pos, int j) __attribute__((always_inline)) {
+    const uint32_t off = j < g ? uint32_t((int64_t(j) * a.logits_ld + pos) * 4) : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), score_rsrc, off, 0, 0);
+  };
+
   auto compute_tile = [&](int k, const Frag& f) __attribute__((always_inline)) {
     const int p0 = logical_tile(first + kWaves * k) * kTile;
     auto attended = [&](int m) __attribute__((always_inline)) { return attended_at(p0, m); };
@@ -430,9 +446,8 @@ void split_kernel(const SplitArgs a) {
       float s[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) s[r] = attended(4 * q4 + r) ? acc[r] * a.scale_log2 : neg_inf();
-      if (SCORES && r16 < g)  // score export: positions p0 + 4*q4 .. +3 of head r16
-        *reinterpret_cast<f32x4_t*>(a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * g + r16) * a.logits_ld +
-                                    p0 + 4 * q4) = f32x4_t{s[0], s[1], s[2], s[3]};
+      if constexpr (SCORES)  // score export: positions p0 + 4*q4 .. +3 of head r16
+        store_scores(f32x4_t{s[0], s[1], s[2], s[3]}, p0 + 4 * q4, r16);
       float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mt = max_xor32(max_xor16(mt));
       const float m_new = fmaxf(m_run, mt);
@@ -465,12 +480,12 @@ void split_kernel(const SplitArgs a) {
           s[i][j] = valid ? x * a.scale_log2 : neg_inf();
         }
       }
-      if constexpr (SCORES) {  // score export: lane r16 = j writes head j's four positions
-        static_for<0, G>([&](auto J) __attribute__((always_inline)) {
-          if (J() < g && r16 == J())
-            *reinterpret_cast<f32x4_t*>(a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * g + J()) * a.logits_ld +
-                                        p0 + 4 * q4) = f32x4_t{s[0][J()], s[1][J()], s[2][J()], s[3][J()]};
+      if constexpr (SCORES) {  // score export: lane r16 writes head r16's four positions
+        f32x4_t v = {s[0][0], s[1][0], s[2][0], s[3][0]};
+        static_for<1, G>([&](auto J) __attribute__((always_inline)) {
+          if (r16 == J()) v = f32x4_t{s[0][J()], s[1][J()], s[2][J()], s[3][J()]};
         });
+        store_scores(v, p0 + 4 * q4, r16);
       }
       bool any_change = false;
       float cv[G];
@@ -815,7 +830,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
 }
 
 // Per-position attention weights (score export): one workgroup per (sequence, KV head, chunk of
-// kScoreChunk positions). The weight of an attended position t for query row j is
+// kScoreChunk positions), reading the split kernel's scores ([B*h_q, logits_ld], one row per
+// query head). The weight of an attended position t for query row j is
 // 2^(s_jt - m_j) / l_j with the row's final base-2 maximum m_j and sum l_j; the group's rows are
 // summed. Unattended positions (past the length, or outside the window) get 0, or are left
 // alone when accumulating.
@@ -893,12 +909,14 @@ int launch_one(const SplitArgs& a, int64_t grid, hipStream_t stream) {
   return int(hipGetLastError());
 }
 
-// Score export: bf16 q and KV on the matrix cores, or fp32 q and KV on the vector path; the
-// cache layout is decided at run time.
+// Score export: bf16 q and KV on the matrix cores (cache layout compiled in, as for the regular
+// kernel), or fp32 q and KV on the vector path (layout decided at run time).
 template <int D, int G>
-int launch_scores_variant(const SplitArgs& a, const Plan& plan, bool q_bf16, bool kv_bf16,
-                          hipStream_t s) {
-  if (plan.variant == 1) return launch_one<D, G, true, true, true, 2, 0, true>(a, plan.grid_split, s);
+int launch_scores_variant(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16,
+                          bool kv_bf16, hipStream_t s) {
+  if (plan.variant == 1)
+    return paged ? launch_one<D, G, true, true, true, 1, 0, true>(a, plan.grid_split, s)
+                 : launch_one<D, G, true, true, true, 0, 0, true>(a, plan.grid_split, s);
   if (!q_bf16 && !kv_bf16) return launch_one<D, G, false, false, false, 2, 0, true>(a, plan.grid_split, s);
   return int(hipErrorInvalidValue);
 }
@@ -918,7 +936,7 @@ int launch_rows(const SplitArgs& a, const Plan& plan, bool paged, hipStream_t s)
 template <int D, int G>
 int launch_dtype(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16, bool kv_bf16,
                  hipStream_t s) {
-  if (a.logits != nullptr) return launch_scores_variant<D, G>(a, plan, q_bf16, kv_bf16, s);
+  if (a.logits != nullptr) return launch_scores_variant<D, G>(a, plan, paged, q_bf16, kv_bf16, s);
   if (plan.variant == 1) {
     return paged ? launch_one<D, G, true, true, true, 1>(a, plan.grid_split, s)
                  : launch_one<D, G, true, true, true, 0>(a, plan.grid_split, s);
