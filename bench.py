@@ -373,6 +373,7 @@ def main():
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "outputs_finite": finite,
         "cpu_baseline": cpu,
+        "context": page_context(A, kv_bytes_step, ms_per_step),
     }
     if args.scores:
         line["config"]["scores"] = ("each layer also writes every attended position's attention "
@@ -385,6 +386,23 @@ def main():
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
     print(json.dumps(line), flush=True)
+
+
+def page_context(A, kv_bytes_step, ms_per_step):
+    """The pages' analytic A100 figures (Ch. 19 §19.2.1 and §19.3.2), quoted as context for the
+    measured step, not as targets: the same unique-KV bytes at A100's bandwidth, and the 7B decode
+    step bound the page derives (weights plus the KV of 1024 tokens, read once per step)."""
+    a100_bw = 1.55e12
+    return {
+        "kind": "the pages' analytic estimates for A100 (context, not targets)",
+        "a100_hbm_tb_s": 1.55,
+        "a100_fp16_tflop_s": 312,
+        "a100_ridge_flop_per_byte": round(A.ridge_point(312e12, a100_bw), 1),
+        "a100_floor_us_for_this_step": round(kv_bytes_step / a100_bw * 1e6, 1),
+        "measured_us_per_step": round(ms_per_step * 1e3, 2),
+        "llama7b_decode_step_bound_ms_a100": round(
+            A.decode_step_bandwidth_bound(7e9, 32, 4096, 1024, a100_bw) * 1e3, 2),
+    }
 
 
 def bench_evict(args, W):
