@@ -125,35 +125,26 @@ __device__ __forceinline__ unsigned long long make_key(float x, uint32_t idx) {
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<unsigned long long>(ord) << 32) | static_cast<unsigned long long>(~idx);
 }
+static_assert(51 >= 32, "the top digit lies in the score word");
 
 __device__ __forceinline__ int digit_of(unsigned long long key, int pass) {
   return int((key >> digit_shift(pass)) & ((1ull << digit_bits(pass)) - 1ull));
 }
 
-// Four consecutive entries i0 .. i0+3 (i0 a multiple of 4). VEC: the four share a row and one
-// aligned 128-bit load reads them. valid: inside the array; pool: valid and not the current
-// position.
+// Four consecutive entries i0 .. i0+3 (i0 a multiple of 4) and whether each is inside the array.
+// VEC: dense rows (row_stride == N) and n a multiple of 4, so the scores are one flat array read
+// with aligned 128-bit loads and no row arithmetic. Otherwise each entry is addressed through its
+// row.
 template <bool VEC>
-__device__ __forceinline__ void load4(const Args& a, int64_t i0, float (&x)[4], bool (&valid)[4],
-                                      bool (&pool)[4]) {
+__device__ __forceinline__ void load4(const Args& a, int64_t i0, float (&x)[4], bool (&valid)[4]) {
   if constexpr (VEC) {
     const bool in = i0 < a.n;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (in) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(a.scores + i0));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       valid[e] = in;
-      x[e] = 0.f;
-      pool[e] = false;
-    }
-    if (in) {
-      const int row = row_of(a, i0);
-      const int t0 = int(i0 - int64_t(row) * a.N);
-      const f32x4_t v = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4_t*>(a.scores + int64_t(row) * a.row_stride + t0));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = v[e];
-        pool[e] = t0 + e != a.current;
-      }
+      x[e] = v[e];
     }
   } else {
 #pragma unroll
@@ -161,15 +152,26 @@ __device__ __forceinline__ void load4(const Args& a, int64_t i0, float (&x)[4], 
       const int64_t i = i0 + e;
       valid[e] = i < a.n;
       x[e] = 0.f;
-      pool[e] = false;
       if (valid[e]) {
         const int row = row_of(a, i);
-        const int t = int(i - int64_t(row) * a.N);
-        x[e] = a.scores[int64_t(row) * a.row_stride + t];
-        pool[e] = t != a.current;
+        x[e] = a.scores[int64_t(row) * a.row_stride + (i - int64_t(row) * a.N)];
       }
     }
   }
+}
+
+// The order-preserving top bits of a score (the high word of its key), without building the key.
+__device__ __forceinline__ uint32_t ord_of(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int top_digit(float x) { return int(ord_of(x) >> (digit_shift(0) - 32)); }
+
+// Whether flat entry i is a row's current position (kept outside the pool).
+__device__ __forceinline__ bool is_current(const Args& a, int64_t i) {
+  return i - int64_t(row_of(a, i)) * a.N == a.current;
 }
 
 // Add a workgroup's LDS histogram into one replica of a global histogram (bins that stayed zero
@@ -249,11 +251,25 @@ __device__ void select_digit(const unsigned int* s_tot, int pass, unsigned long 
   __syncthreads();
 }
 
+// Clears the histograms. The passes histogram every entry, current positions included; to leave
+// the pool's histogram, workgroup 0 starts replica 0 of the top-digit histogram at minus the
+// current positions' counts (unsigned wrap-around cancels exactly once they are added).
 __global__ __launch_bounds__(256) void init_kernel(const Args a) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);  // one 16-byte piece
-  constexpr int kPieces = (kReplicas0 + kReplicas1) * kBins / 4;
-  if (i < kPieces) reinterpret_cast<u32x4_t*>(a.hist0)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  __shared__ unsigned int h[kBins];
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0u;
+    __syncthreads();
+    const int64_t rows = a.n / a.N;
+    for (int64_t r = threadIdx.x; r < rows; r += 256)
+      atomicAdd(&h[top_digit(a.scores[r * a.row_stride + a.current])], 1u);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kBins; i += 256) a.hist0[i] = 0u - h[i];
+    return;
+  }
+  const int i = int(blockIdx.x - 1) * 256 + int(threadIdx.x);  // one 16-byte piece past replica 0
+  constexpr int kPieces = (kReplicas0 + kReplicas1 - 1) * kBins / 4;
+  if (i < kPieces) reinterpret_cast<u32x4_t*>(a.hist0 + kBins)[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
 // Pass 0: histogram of the top digit over the whole pool.
@@ -264,16 +280,15 @@ __global__ __launch_bounds__(kStreamThreads) void pass0_kernel(const Args a) {
   __syncthreads();
   for (int64_t base = int64_t(blockIdx.x) * kChunk; base < a.n; base += int64_t(gridDim.x) * kChunk) {
     float x[kSlabs][4];
-    bool valid[kSlabs][4], pool[kSlabs][4];
+    bool valid[kSlabs][4];
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s)
-      load4<VEC>(a, base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec, x[s], valid[s], pool[s]);
+      load4<VEC>(a, base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec, x[s], valid[s]);
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
-      const int64_t i0 = base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (pool[s][e]) atomicAdd(&h[digit_of(make_key(x[s][e], uint32_t(i0 + e)), 0)], 1u);
+        if (valid[s][e]) atomicAdd(&h[top_digit(x[s][e])], 1u);
     }
   }
   __syncthreads();
@@ -305,25 +320,24 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(const Args a) {
   unsigned long long* region = a.list1 + int64_t(blockIdx.x) * a.cap1;
   for (int64_t base = int64_t(blockIdx.x) * kChunk; base < a.n; base += int64_t(gridDim.x) * kChunk) {
     float x[kSlabs][4];
-    bool valid[kSlabs][4], pool[kSlabs][4];
+    bool valid[kSlabs][4];
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s)
-      load4<VEC>(a, base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec, x[s], valid[s], pool[s]);
+      load4<VEC>(a, base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec, x[s], valid[s]);
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
       const int64_t i0 = base + s * (kStreamThreads * kVec) + int(threadIdx.x) * kVec;
       uint32_t m[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        m[e] = valid[s][e] ? 1u : 0u;  // current positions stay
-        if (pool[s][e]) {
+        // Current positions get their 1 from the final kernel; only the rare entries that share
+        // k*'s top digit check whether they are one (and then stay out of the lists).
+        const int d = top_digit(x[s][e]);
+        m[e] = valid[s][e] && d > d0 ? 1u : 0u;
+        if (valid[s][e] && d == d0 && !is_current(a, i0 + e)) {
           const unsigned long long key = make_key(x[s][e], uint32_t(i0 + e));
-          const int d = digit_of(key, 0);
-          m[e] = d > d0 ? 1u : 0u;
-          if (d == d0) {
-            region[atomicAdd(&s_n, 1u)] = key;
-            atomicAdd(&h[digit_of(key, 1)], 1u);
-          }
+          region[atomicAdd(&s_n, 1u)] = key;
+          atomicAdd(&h[digit_of(key, 1)], 1u);
         }
       }
       if constexpr (VEC) {
@@ -429,6 +443,9 @@ __global__ __launch_bounds__(kFinishThreads) void final_kernel(const Args a) {
     const unsigned long long key = entry(j);
     if (key >= kstar) a.keep[~static_cast<uint32_t>(key)] = 1u;
   }
+  // Rule 1: every row's current position stays (pass 1 gave it the value of its top digit).
+  const int64_t rows = a.n / a.N;
+  for (int64_t r = threadIdx.x; r < rows; r += kFinishThreads) a.keep[r * a.N + a.current] = 1u;
 }
 
 // The budget alone decides: all = 0 keeps only the current positions, all = 1 keeps everything.
@@ -563,10 +580,11 @@ kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept
                        a, all);
     if (hipGetLastError() != hipSuccess) return KV_ATTN_ERR_HIP;
   } else {
-    const bool vec = p->num_tokens % 4 == 0 && p->row_stride % 4 == 0 && aligned(scores, 16) &&
+    const bool vec = p->row_stride == p->num_tokens && a.n % 4 == 0 && aligned(scores, 16) &&
                      aligned(keep, 4);
-    hipLaunchKernelGGL(init_kernel, dim3(((kReplicas0 + kReplicas1) * kBins / 4 + 255) / 256),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL(init_kernel,
+                       dim3(1 + ((kReplicas0 + kReplicas1 - 1) * kBins / 4 + 255) / 256), dim3(256),
+                       0, s, a);
     if (vec) {
       hipLaunchKernelGGL(pass0_kernel<true>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
       hipLaunchKernelGGL(pass1_kernel<true>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
