@@ -95,6 +95,9 @@ def parse_args():
     ap.add_argument("--gamma", type=int, default=1,
                     help="query tokens per sequence (speculative-decoding verification: the last "
                          "gamma cached positions, causal among themselves)")
+    ap.add_argument("--block-order", choices=["random", "sequential"], default=None,
+                    help="paged workloads: deal the physical blocks to the sequences in a random "
+                         "order (the workload's default) or in physical order")
     ap.add_argument("--scores", action="store_true",
                     help="each layer also exports the attention weight of every cached position "
                          "(kv_attn_decode_scores)")
@@ -145,6 +148,13 @@ def main():
     elif args.attn_sinks is not None:
         print("bench.py: --attn-sinks needs --window", file=sys.stderr)
         sys.exit(2)
+    if args.block_order is not None:
+        if not spec.paged:
+            print("bench.py: --block-order needs a paged workload (C4, C5)", file=sys.stderr)
+            sys.exit(2)
+        spec = dataclasses.replace(spec, block_order=args.block_order)
+        if args.block_order != "random":
+            tag = f"{tag}_{args.block_order}"
     if args.gamma < 1:
         print("bench.py: --gamma must be >= 1", file=sys.stderr)
         sys.exit(2)
@@ -343,6 +353,8 @@ def main():
             "workload": f"{spec.name}: {spec.description}" + (
                 f"; sliding window of {spec.window} positions plus the first {spec.num_sinks} "
                 "(attention sinks), the rest NaN-poisoned and never read" if spec.window else "")
+                + ("; blocks dealt to the sequences in physical order"
+                   if spec.paged and spec.block_order == "sequential" else "")
                 + (f"; {gamma} query tokens per sequence (speculative-decoding verification: the "
                    "last gamma cached positions, causal among themselves)" if gamma > 1 else ""),
             "num_queries": gamma,
@@ -352,6 +364,7 @@ def main():
             "sum_attended_len": sum(att),
             "layers": layers, "kv_dtype": spec.kv_dtype, "q_dtype": spec.q_dtype,
             "paged": spec.paged, "layout": spec.layout,
+            "block_order": spec.block_order if spec.paged else None,
             "unique_kv_bytes_per_step": kv_bytes_step, "flops_per_step": flops_step,
             "plan": {k: plan[k] for k in ("num_splits", "split_len", "grid_split", "grid_merge",
                                           "kernel_variant", "num_cus")},

@@ -215,13 +215,16 @@ void split_kernel(const SplitArgs a) {
   // consecutive indices are different (sequence, KV head) units of the same split, so every
   // XCD receives the same mix of early (always full) and late (often empty) splits; with the
   // split index fastest, XCD k would get split k of every unit and ragged batches would load
-  // the XCDs very unevenly.
+  // the XCDs very unevenly. Within a split the KV head is rotated by the split index: when
+  // h_kv is a multiple of 8, XCD k would otherwise see only KV heads k, k+8, ..., and with a
+  // head-major paged cache whose blocks a sequence holds in physical order each XCD would read
+  // the same few 4 KiB slices of every block (measured on MI355X: 0.67 of peak instead of 0.79).
   const int S = a.num_splits;
   const int units = int(gridDim.x) / S;
   const int split = blockIdx.x / units;
   const int unit = blockIdx.x - split * units;
-  const int kvh = unit % a.h_kv;
   const int b = unit / a.h_kv;
+  const int kvh = (unit - b * a.h_kv + split) % a.h_kv;
   const int g = a.group;
   const bool paged = PAGED == 2 ? (a.block_table != nullptr) : (PAGED == 1);
 

@@ -81,6 +81,10 @@ class WorkloadSpec:
     # the last gamma cached positions (a speculative draft being checked); the window poisoning
     # then spares the union of the gamma tokens' windows.
     num_queries: int = 1
+    # Paged: "random" deals the physical blocks to the sequences in a seeded random order;
+    # "sequential" gives every sequence a run of consecutive physical blocks, as a fresh
+    # allocator hands them out.
+    block_order: str = "random"
     description: str = ""
 
     @property
@@ -188,7 +192,8 @@ def workload_structure(spec: WorkloadSpec, layer: int = 0) -> dict:
     """Context lengths, block table and storage shape of ``spec`` (no K/V values), on the CPU.
 
     Paged caches: every sequence gets ceil(T_b / block_size) physical blocks, taken in order
-    from a seeded random permutation of all physical blocks; the blocks left over (at least one)
+    from a seeded random permutation of all physical blocks (``block_order="sequential"``: from
+    the blocks in physical order); the blocks left over (at least one)
     are never referenced by a live table entry, and table entries past a sequence's last block
     point at one of them (it is NaN-poisoned, so a stray read shows up in the output).
     """
@@ -204,7 +209,12 @@ def workload_structure(spec: WorkloadSpec, layer: int = 0) -> dict:
         nblk = [(int(t) + bs - 1) // bs for t in ctx.tolist()]
         used = sum(nblk)
         total = used + max(1, spec.extra_blocks)
-        perm = torch.randperm(total, generator=_generator(seed, 3, "cpu")).to(torch.int32)
+        if spec.block_order == "random":
+            perm = torch.randperm(total, generator=_generator(seed, 3, "cpu")).to(torch.int32)
+        elif spec.block_order == "sequential":
+            perm = torch.arange(total, dtype=torch.int32)
+        else:
+            raise ValueError(f"block_order {spec.block_order!r}")
         poison_block = int(perm[used].item())
         table = torch.full((B, max(1, max(nblk))), poison_block, dtype=torch.int32)
         off = 0

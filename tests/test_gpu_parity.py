@@ -34,6 +34,9 @@ SMALL = [
     ("C4", dict(batch=6, ctx=("uniform", 1, 700))),
     ("C4", dict(batch=5, ctx=("uniform", 1, 300), layout="token_major", extra_blocks=7)),
     ("C5", dict(batch=2, ctx=(3000, 2999))),
+    ("C5", dict(batch=3, ctx=(3000, 1, 2999), block_order="sequential")),
+    ("C4", dict(batch=6, ctx=("uniform", 1, 700), block_order="sequential", num_kv_heads=16,
+                num_q_heads=32)),
 ]
 
 
@@ -102,6 +105,7 @@ FULL = [
     ("C3", [0, 63], [0, 7]),
     ("C4", "extremes", [0, 7]),
     ("C5", [0, 3], [0, 5]),
+    ("C5-sequential", [1, 2], [3, 7]),
 ]
 
 
@@ -110,10 +114,13 @@ def test_full_size_workloads_on_sampled_rows(name, seqs, heads):
     """The bench's launch configuration (auto split plan) at full size; sampled rows checked.
 
     C4 samples its shortest, longest and a middle sequence. C2 is one of its 32 layers.
+    C5-sequential deals the blocks to the sequences in physical order.
     """
     require_gpu()
     announce(f"full {name}")
-    w = W.make_workload(W.PRESETS[name], device="cuda")
+    base, _, order = name.partition("-")
+    spec = W.preset(base, block_order=order) if order else W.PRESETS[base]
+    w = W.make_workload(spec, device="cuda")
     try:
         out = run(w)
         if seqs is None:

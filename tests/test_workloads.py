@@ -55,8 +55,21 @@ def test_c4_full_structure():
     assert np.mean(np.diff(live) == 1) < 0.01
 
 
-def test_paged_tails_and_unused_blocks_are_poisoned():
-    w = W.make_workload(_small("C4", extra_blocks=3))
+def test_sequential_block_order_gives_each_sequence_a_physical_run():
+    st = W.workload_structure(W.preset("C4", block_order="sequential", extra_blocks=2))
+    ctx = st["ctx"].numpy()
+    table = st["table"].numpy()
+    nblk = (ctx + 15) // 16
+    live = np.concatenate([table[b, :n] for b, n in enumerate(nblk)])
+    assert np.array_equal(live, np.arange(nblk.sum()))
+    assert st["unused_blocks"] == [int(nblk.sum()), int(nblk.sum()) + 1]
+    with pytest.raises(ValueError):
+        W.workload_structure(W.preset("C4", block_order="shuffled"))
+
+
+@pytest.mark.parametrize("order", ["random", "sequential"])
+def test_paged_tails_and_unused_blocks_are_poisoned(order):
+    w = W.make_workload(_small("C4", extra_blocks=3, block_order=order))
     view = W.oracle_view(w)
     k = view["k_cache"]
     bits = k.view(np.uint16) if k.dtype == np.uint16 else None
