@@ -132,7 +132,9 @@ typedef struct kv_attn_plan {
   int32_t grid_merge;       /* workgroups of the merge kernel: batch * num_queries *
                                num_q_heads (0 when S == 1) */
   int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores,
-                               2: bf16 MFMA scores and P.V for num_queries > 1 */
+                               2: bf16 MFMA scores and P.V ("rows mode": num_queries > 1, or
+                               one token with a group of 4 or more query heads per KV head;
+                               kv_attn_decode_scores runs variant 1 in its place) */
   int32_t group_padded;     /* compiled group width (power of two >= g) */
   int32_t num_cus;          /* compute units the plan was made for */
   int32_t reserved;

@@ -25,6 +25,7 @@ constexpr int kWorkgroupsPerCu = 1;    // target split workgroups per compute un
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxQueryRows = 32;      // rows mode: num_queries * group <= 32 (two MFMA blocks)
 constexpr int kMaxQueries = 16;
+constexpr int kRowsMinGroup = 4;      // one query token: rows mode from this group size on (bf16)
 
 // Everything the split kernel needs, by value.
 struct SplitArgs {

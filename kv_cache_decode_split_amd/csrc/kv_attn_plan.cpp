@@ -131,11 +131,16 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   const int32_t nq = num_queries(p);
   plan->num_queries = nq;
   plan->row_blocks = 0;
-  if (nq > 1) {
+  const int32_t g = p->num_q_heads / p->num_kv_heads;
+  const bool bf16 = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector;
+  // Rows mode (variant 2) also serves one token once the group has kRowsMinGroup heads: P.V
+  // then costs less on the matrix cores than as per-lane FMAs for every head (on MI355X the
+  // C5 shape, group 8, went from 0.79 to 0.82 of peak, at the bandwidth of the loads alone).
+  if (nq > 1 || (bf16 && g >= kRowsMinGroup)) {
     plan->variant = 2;
-    plan->row_blocks = int32_t(ceil_div(int64_t(nq) * (p->num_q_heads / p->num_kv_heads), 16));
+    plan->row_blocks = int32_t(ceil_div(int64_t(nq) * g, 16));
   } else {
-    plan->variant = (p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector) ? 1 : 0;
+    plan->variant = bf16 ? 1 : 0;
   }
   plan->grid_split = units * S;
   const int64_t rows = int64_t(p->batch) * nq * p->num_q_heads;

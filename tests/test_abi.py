@@ -198,7 +198,8 @@ def test_plan_for_the_five_workloads():
                     max_blocks_per_seq=(T + 15) // 16, num_blocks=10**6)
         plan = K.kv_attn_get_plan(p, 256)
         assert (plan["num_splits"], plan["split_len"]) == (S, L)
-        assert plan["kernel_variant"] == 1
+        # groups of 4 or more run P.V on the matrix cores too (rows mode)
+        assert plan["kernel_variant"] == (2 if hq // hkv >= 4 else 1)
 
 
 def test_explicit_split_count_and_variant_selection():
@@ -209,6 +210,11 @@ def test_explicit_split_count_and_variant_selection():
     assert K.kv_attn_get_plan(p, 256)["kernel_variant"] == 0
     p = _params(num_q_heads=8 * 3)
     assert K.kv_attn_get_plan(p, 256)["group_padded"] == 4
+    assert K.kv_attn_get_plan(p, 256)["kernel_variant"] == 1
+    for g in (4, 5, 16):
+        assert K.kv_attn_get_plan(_params(num_q_heads=8 * g), 256)["kernel_variant"] == 2, g
+    p = _params(num_q_heads=8 * 8, q_dtype=K.KV_ATTN_F32, kv_dtype=K.KV_ATTN_F32)
+    assert K.kv_attn_get_plan(p, 256)["kernel_variant"] == 0
 
 
 def _decode_raw(p, q=16, k=16, v=16, bt=16, ctx=16, out=16, ws=None, ws_bytes=0):

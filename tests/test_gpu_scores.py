@@ -1,8 +1,10 @@
 """GPU parity of decode with score export (kv_attn_decode_scores) against the fp64 oracle.
 
 The exported weights are compared with ``oracle.position_scores`` at the parity tolerance; the
-attention output of the same call must equal plain kv_attn_decode bit for bit (the export only
-adds stores); accumulation adds exactly and leaves unattended entries alone; and a decode ->
+attention output of the same call must equal plain kv_attn_decode bit for bit where both run
+the same kernel (the export only adds stores; plain decode of bf16 groups of 4 or more runs the
+rows-mode kernel instead, and the output is then compared with the oracle); accumulation adds
+exactly and leaves unattended entries alone; and a decode ->
 scores -> eviction pipeline over several layers selects exactly what the oracle selection picks
 from the same scores.
 """
@@ -12,7 +14,7 @@ import pytest
 import torch
 
 from kv_cache_decode_split_amd import workloads as W
-from tests.gpu_helpers import announce, check_close, require_gpu, run
+from tests.gpu_helpers import announce, check_close, oracle_full, require_gpu, run
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +27,17 @@ def _oracle_scores(w, seqs=None, kv_heads=None):
     return position_scores(v["q"], v["k_cache"], v["ctx_lens"], v["block_table"],
                            block_size=v["block_size"] if paged else None,
                            max_len=w.max_ctx_len, **kw)
+
+
+def _check_output(out, w, num_splits, label):
+    """The output of a score-export call: the plain decode's bits when that runs the same
+    one-token kernel, else within the parity tolerance of the oracle."""
+    K = require_gpu()
+    plain_call = K.decode_call_for(w, torch.empty_like(out), num_splits=num_splits)
+    if plain_call.plan()["kernel_variant"] != 2:
+        assert torch.equal(out, run(w, num_splits=num_splits)), "score export changed the output"
+    else:
+        check_close(out.cpu().numpy(), oracle_full(w), f"{label} output")
 
 
 def _run_scores(w, accumulate=False, fill=float("nan"), **kwargs):
@@ -60,8 +73,7 @@ def test_exported_weights_match_oracle(name, over, num_splits):
     out, scores = _run_scores(w, num_splits=num_splits)
     ref = _oracle_scores(w)
     check_close(scores.cpu().numpy(), ref, f"scores {name} S={num_splits}")
-    plain = run(w, num_splits=num_splits)
-    assert torch.equal(out, plain), "score export changed the attention output"
+    _check_output(out, w, num_splits, f"scores {name} S={num_splits}")
     lens = w.ctx_lens.cpu().numpy()
     sums = scores.double().sum(-1).cpu().numpy()
     for b, length in enumerate(lens):
@@ -202,4 +214,4 @@ def test_random_shapes_export_oracle_weights(case):
     w = W.make_workload(spec, device="cuda")
     out, scores = _run_scores(w, num_splits=case["num_splits"])
     check_close(scores.cpu().numpy(), _oracle_scores(w), f"{spec.name} scores")
-    assert torch.equal(out, run(w, num_splits=case["num_splits"]))
+    _check_output(out, w, case["num_splits"], spec.name)
