@@ -538,17 +538,20 @@ void split_kernel(const SplitArgs a) {
 
   // Rows mode: scores S^T[key][row] = K Q^T and O^T[d][row] += V^T P^T, both on the matrix cores.
   // The score MFMA leaves, in lane (q4, r16), the scores of keys 4*q4 .. 4*q4+3 for query row
-  // r16 of the block, which is exactly the lane layout of the B operand P^T of a 16x16x16 MFMA.
-  // For the A operand V^T the d index of output row m of block dc is taken as EPL*m + dc, so
-  // that lane (q4, r16) needs V[4*q4 + i][EPL*r16 + dc], i = 0..3: elements this lane already
-  // loaded (value rows 4*q4+i, elements EPL*r16 ..), repacked with no data exchange between
-  // lanes. The bf16 operand cannot hold P to fp32 accuracy (a lone probability near 1 would
-  // carry up to 2^-8 relative error into the output), so P is split into p_hi = bf16(p) and
-  // p_lo = bf16(p - p_hi) and both halves are multiplied in: the product then matches fp32 P to
-  // 2^-16 relative, and l keeps the fp32 probabilities.
+  // r16 of the block. The bf16 operand cannot hold P to fp32 accuracy (a lone probability near 1
+  // would carry up to 2^-8 relative error into the output), so P is split into p_hi = bf16(p) and
+  // p_lo = bf16(p - p_hi) (together within 2^-16 relative of p; l keeps the fp32 probabilities),
+  // and both halves go through one 16x16x32 MFMA: its 32 k-slots hold the tile's 16 keys twice.
+  // Lane (q4, r16) supplies k-slots 8*q4 .. 8*q4+7, taken as keys 4*q4 + (e & 3) of half e >> 2:
+  // B gets (p_hi, p_lo) of its four keys, exactly the values the score MFMA left in the lane,
+  // and A = V^T gets the same four value rows twice. For A the d index of output row m of block
+  // dc is taken as EPL*m + dc, so that lane (q4, r16) needs V[4*q4 + i][EPL*r16 + dc], i = 0..3:
+  // elements it already loaded (value rows 4*q4+i, elements EPL*r16 ..), repacked with no data
+  // exchange between lanes. (On MI355X one 16x16x32 MFMA issues in about 1.14 times the cycles
+  // of a 16x16x16 one, which the two halves would otherwise need twice.)
   auto compute_rows = [&](int k, const Frag& f) __attribute__((always_inline)) {
     const int p0 = logical_tile(first + kWaves * k) * kTile;
-    bf16x4_t vt[EPL];
+    bf16x8_t vt[EPL];
 #pragma unroll
     for (int dc = 0; dc < EPL; ++dc) {
       const int w = dc >> 1;
@@ -560,7 +563,7 @@ void split_kernel(const SplitArgs a) {
         lo = (f.vr[0].w[w] & 0xffffu) | (f.vr[1].w[w] << 16);
         hi = (f.vr[2].w[w] & 0xffffu) | (f.vr[3].w[w] << 16);
       }
-      vt[dc] = __builtin_bit_cast(bf16x4_t, u32x2_t{lo, hi});
+      vt[dc] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo, hi, lo, hi});
     }
 #pragma unroll
     for (int cb = 0; cb < RB; ++cb) {
@@ -597,14 +600,10 @@ void split_kernel(const SplitArgs a) {
       const f32x4_t hi_f = __builtin_convertvector(p_hi, f32x4_t);
       const bf16x4_t p_lo = __builtin_convertvector(
           f32x4_t{pf[0] - hi_f[0], pf[1] - hi_f[1], pf[2] - hi_f[2], pf[3] - hi_f[3]}, bf16x4_t);
-      // The two chains are issued one after the other so that consecutive MFMAs write different
-      // accumulators.
+      const bf16x8_t p_b = __builtin_shufflevector(p_hi, p_lo, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int dc = 0; dc < EPL; ++dc)
-        oT[cb][dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[dc], p_hi, oT[cb][dc], 0, 0, 0);
-#pragma unroll
-      for (int dc = 0; dc < EPL; ++dc)
-        oT[cb][dc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[dc], p_lo, oT[cb][dc], 0, 0, 0);
+        oT[cb][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[dc], p_b, oT[cb][dc], 0, 0, 0);
     }
   };
   auto compute = [&](int k, const Frag& f) __attribute__((always_inline)) {
