@@ -26,12 +26,16 @@
 //  * Both variants accumulate P.V in fp32 on the vector ALUs: lane (r, q4) owns elements
 //    [r*d/16, (r+1)*d/16) of the value rows 4*q4 .. 4*q4+3 of the tile, and takes the
 //    probabilities it needs by DPP row broadcast (variant 1) or directly (variant 0).
+//  * rows mode (variant 2: several query tokens per sequence, or one token with a bf16 group
+//    of 4 or more heads): up to 32 query rows per KV head in one or two blocks of 16 MFMA
+//    columns; scores as in variant 1, and P.V on the matrix cores as well (see compute_rows).
 //
 // Loads are 64- to 128-bit per lane; the tile's key rows are 16 contiguous 64-byte pieces per
 // instruction (MFMA operand layout), value rows are whole 256-byte rows per 16 lanes. Tiles
 // are double-buffered in registers so the next tile's loads are in flight while the current
-// one is computed. Positions past the sequence end are never read: their row index is clamped
-// to the last valid row and the score is masked to -inf.
+// one is computed (two-block rows mode keeps one tile in flight, to fit two waves per SIMD).
+// Positions that are not attended are never read: their row index is redirected to an attended
+// row of the same tile and the score is masked to -inf.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
