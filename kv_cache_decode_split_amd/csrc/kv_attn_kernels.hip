@@ -555,6 +555,12 @@ void split_kernel(const SplitArgs a) {
   // of a 16x16x16 one, which the two halves would otherwise need twice.)
   auto compute_rows = [&](int k, const Frag& f) __attribute__((always_inline)) {
     const int p0 = logical_tile(first + kWaves * k) * kTile;
+    // Most tiles are attended by every query row at all 16 positions (below the first token's
+    // limit, and all sinks or all at or past the last token's window start): they skip the
+    // per-row masks. (Padding rows then see real scores of their zero query; they are never
+    // written out.)
+    const bool open = p0 + kTile <= ctx - nq + 1 &&
+                      (a.window <= 0 || p0 >= ctx - a.window || p0 + kTile <= snk);
     bf16x8_t vt[EPL];
 #pragma unroll
     for (int dc = 0; dc < EPL; ++dc) {
@@ -577,11 +583,16 @@ void split_kernel(const SplitArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.kc[c]),
                                                       qb[cb][c], acc, 0, 0, 0);
       float sc[4];
+      if (open) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = p0 + 4 * q4 + r;
-        const bool valid = pos < lim[cb] && (pos < snk || pos >= wst[cb]);
-        sc[r] = valid ? acc[r] * a.scale_log2 : neg_inf();
+        for (int r = 0; r < 4; ++r) sc[r] = acc[r] * a.scale_log2;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = p0 + 4 * q4 + r;
+          const bool valid = pos < lim[cb] && (pos < snk || pos >= wst[cb]);
+          sc[r] = valid ? acc[r] * a.scale_log2 : neg_inf();
+        }
       }
       float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mt = max_xor32(max_xor16(mt));
