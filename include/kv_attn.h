@@ -100,7 +100,7 @@ typedef enum kv_attn_dtype {
  *            block_size is then the token capacity of one sequence slot.
  */
 typedef struct kv_attn_params {
-  int32_t batch;              /* B >= 1 */
+  int32_t batch;              /* B >= 1; B * gamma * h_kv * head_dim * elem_bytes / 16 < 2^31 */
   int32_t num_q_heads;        /* h_q >= 1 */
   int32_t num_kv_heads;       /* h_kv >= 1, h_q % h_kv == 0, 1 <= h_q / h_kv <= 16 */
   int32_t head_dim;           /* d: 64 or 128 */

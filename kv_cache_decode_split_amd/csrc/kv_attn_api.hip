@@ -139,8 +139,6 @@ AppendArgs append_args(const kv_attn_params* p, const void* k_new, const void* v
   return a;
 }
 
-// Shared body of kv_attn_decode / _split / _merge: validation, planning, then the passes in
-// `passes`. Every host-side check runs before the first HIP call.
 // Score export (token_scores != nullptr): where the logits and row statistics go in the workspace.
 struct ScoreLayout {
   uint64_t logits_offset, stats_offset, total;
@@ -160,6 +158,8 @@ ScoreLayout score_layout(const kv_attn_params* p, const Plan& plan) {
   return l;
 }
 
+// Shared body of kv_attn_decode / _split / _merge / _append_decode / _decode_scores: validation,
+// planning, then the passes in `passes`. Every host-side check runs before the first HIP call.
 kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* ctx_lens, float* out,
                            const kv_attn_params* p, void* workspace, size_t workspace_bytes,

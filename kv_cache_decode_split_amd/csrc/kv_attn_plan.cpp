@@ -56,6 +56,11 @@ kv_attn_status validate_params(const kv_attn_params* p) {
   if (p->k_stride_token * eb * kTile >= (int64_t(1) << 31) ||
       p->v_stride_token * eb * kTile >= (int64_t(1) << 31))
     return KV_ATTN_ERR_UNSUPPORTED;
+  // The append kernel numbers its 16-byte pieces (sequence, query token, KV head, piece of a
+  // row) with 32-bit indices.
+  const int64_t pieces = int64_t(p->batch) * (p->num_queries > 1 ? p->num_queries : 1) *
+                         p->num_kv_heads * (p->head_dim * eb / 16);
+  if (pieces > int64_t(INT32_MAX)) return KV_ATTN_ERR_UNSUPPORTED;
   return KV_ATTN_OK;
 }
 

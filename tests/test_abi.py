@@ -80,6 +80,7 @@ def _params(**kw):
     (dict(batch=0), K.KV_ATTN_ERR_SHAPE),
     (dict(num_q_heads=30), K.KV_ATTN_ERR_SHAPE),            # not a multiple of h_kv
     (dict(num_q_heads=8 * 17), K.KV_ATTN_ERR_UNSUPPORTED),  # group 17 > 16
+    (dict(batch=1 << 24, num_queries=2), K.KV_ATTN_ERR_UNSUPPORTED),  # 2^31 append pieces
     (dict(head_dim=96), K.KV_ATTN_ERR_UNSUPPORTED),
     (dict(q_dtype=5), K.KV_ATTN_ERR_UNSUPPORTED),
     (dict(k_strides=(8 * 16 * 128, 127, 16 * 128)), K.KV_ATTN_ERR_UNSUPPORTED),  # misaligned rows
