@@ -20,8 +20,8 @@ constexpr int kSplitThreads = 64 * kWaves;
 constexpr int kMergeThreads = 256;
 // Split planning constants (see make_plan).
 constexpr int kMinSplitTiles = 16;     // a split spans at least 256 positions ...
-constexpr int kMaxSplitTiles = 256;    // ... and at most 4096 positions
-constexpr int kWorkgroupsPerCu = 1;    // target split workgroups per compute unit
+constexpr int kMaxSplitTiles = 256;    // ... and at most 4096 positions with many units ...
+constexpr int kMaxSplitTilesLong = 512;  // ... or 8192 with few units or several query tokens
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxQueryRows = 32;      // rows mode: num_queries * group <= 32 (two MFMA blocks)
 constexpr int kMaxQueries = 16;

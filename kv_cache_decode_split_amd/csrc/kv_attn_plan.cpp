@@ -112,13 +112,39 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   }
   const int64_t tiles_max = max_visited_tiles(p);
   const int64_t units = int64_t(p->batch) * p->num_kv_heads;
+  const bool force_vector = getenv("KV_ATTN_FORCE_VECTOR") != nullptr &&
+                            strcmp(getenv("KV_ATTN_FORCE_VECTOR"), "1") == 0;
+  const int32_t nq = num_queries(p);
+  const int32_t g = p->num_q_heads / p->num_kv_heads;
+  const bool bf16 = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector;
+  plan->num_queries = nq;
+  plan->row_blocks = 0;
+  // Rows mode (variant 2) also serves one token once the group has kRowsMinGroup heads: P.V
+  // then costs less on the matrix cores than as per-lane FMAs for every head (on MI355X the
+  // C5 shape, group 8, went from 0.79 to 0.82 of peak, at the bandwidth of the loads alone).
+  if (nq > 1 || (bf16 && g >= kRowsMinGroup)) {
+    plan->variant = 2;
+    plan->row_blocks = int32_t(ceil_div(int64_t(nq) * g, 16));
+  } else {
+    plan->variant = bf16 ? 1 : 0;
+  }
+
   int64_t S;
   if (p->num_splits > 0) {
     S = p->num_splits;
   } else {
-    S = ceil_div(int64_t(num_cus) * kWorkgroupsPerCu, units);
-    const int64_t most = ceil_div(tiles_max, kMinSplitTiles);   // splits of >= 16 tiles
-    const int64_t least = ceil_div(tiles_max, kMaxSplitTiles);  // splits of <= 256 tiles
+    // About one split workgroup per CU; two for two-block rows mode, which keeps one tile in
+    // flight per wave and needs two waves per SIMD to keep enough loads outstanding.
+    const int64_t per_cu = plan->row_blocks == 2 ? 2 : 1;
+    S = ceil_div(int64_t(num_cus) * per_cu, units);
+    // Split length cap: 256 tiles keep a batch of many (sequence, KV head) units balanced when
+    // its lengths are ragged; with few units (long sequences split for parallelism) or several
+    // query tokens (heavier per-split epilogue and merge rows) 512 tiles stream faster. MI355X
+    // sweeps: C4 (1024 units, ragged) best at 256; C5 (32 units) 0.825 at 512 against 0.815;
+    // C3 with 8 tokens 0.828 against 0.776, C5 with 4 tokens 0.807 against 0.755.
+    const int64_t cap = (nq > 1 || units * 2 < num_cus) ? kMaxSplitTilesLong : kMaxSplitTiles;
+    const int64_t most = ceil_div(tiles_max, kMinSplitTiles);  // splits of >= 16 tiles
+    const int64_t least = ceil_div(tiles_max, cap);
     if (S > most) S = most;
     if (S < least) S = least;
   }
@@ -130,23 +156,7 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
 
   plan->num_splits = int32_t(S);
   plan->split_tiles = int32_t(split_tiles);
-  plan->group_padded = padded_group(p->num_q_heads / p->num_kv_heads);
-  const bool force_vector = getenv("KV_ATTN_FORCE_VECTOR") != nullptr &&
-                            strcmp(getenv("KV_ATTN_FORCE_VECTOR"), "1") == 0;
-  const int32_t nq = num_queries(p);
-  plan->num_queries = nq;
-  plan->row_blocks = 0;
-  const int32_t g = p->num_q_heads / p->num_kv_heads;
-  const bool bf16 = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector;
-  // Rows mode (variant 2) also serves one token once the group has kRowsMinGroup heads: P.V
-  // then costs less on the matrix cores than as per-lane FMAs for every head (on MI355X the
-  // C5 shape, group 8, went from 0.79 to 0.82 of peak, at the bandwidth of the loads alone).
-  if (nq > 1 || (bf16 && g >= kRowsMinGroup)) {
-    plan->variant = 2;
-    plan->row_blocks = int32_t(ceil_div(int64_t(nq) * g, 16));
-  } else {
-    plan->variant = bf16 ? 1 : 0;
-  }
+  plan->group_padded = padded_group(g);
   plan->grid_split = units * S;
   const int64_t rows = int64_t(p->batch) * nq * p->num_q_heads;
   plan->grid_merge = S > 1 ? rows : 0;

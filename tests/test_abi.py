@@ -132,8 +132,12 @@ def test_plan_with_several_query_tokens(nq, hq, hkv):
     one = K.kv_attn_get_plan(_params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
                                      max_blocks_per_seq=T // 16, num_blocks=10**6), 256)
     assert plan["kernel_variant"] == 2
-    assert (plan["num_splits"], plan["split_len"]) == (one["num_splits"], one["split_len"])
-    S = plan["num_splits"]
+    S, L = plan["num_splits"], plan["split_len"]
+    assert L % 16 == 0 and S * L >= T and (S - 1) * L < T
+    assert L <= 8192 and one["split_len"] <= 8192   # splits of at most 512 tiles
+    # two row blocks keep one tile in flight per wave: about two workgroups per CU
+    per_cu = 2 if nq * (hq // hkv) > 16 else 1
+    assert plan["grid_split"] == B * hkv * S >= per_cu * 256
     if S > 1:
         assert plan["grid_merge"] == B * nq * hq
         assert plan["workspace_bytes"] >= B * nq * hq * S * (128 + 2) * 4
@@ -182,7 +186,9 @@ def test_plan_covers_every_tile_and_respects_bounds():
                 assert plan["grid_merge"] == B * hkv * 2
             else:
                 assert plan["workspace_bytes"] == 0 and plan["grid_merge"] == 0
-            assert L // 16 <= 256 or S == 4096
+            # at most 256 tiles per split with many (sequence, KV head) units, 512 with few
+            cap = 512 if B * hkv * 2 < cus else 256
+            assert L // 16 <= cap or S == 4096
 
 
 def test_plan_for_the_five_workloads():
@@ -192,7 +198,7 @@ def test_plan_for_the_five_workloads():
         (8, 32, 32, 4096): (1, 4096),
         (64, 32, 8, 8192): (2, 4096),
         (128, 32, 8, 32768): (8, 4096),
-        (4, 64, 8, 131072): (32, 4096),
+        (4, 64, 8, 131072): (16, 8192),    # few units: splits of up to 512 tiles
     }
     for (B, hq, hkv, T), (S, L) in want.items():
         p = _params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
