@@ -426,22 +426,36 @@ __global__ __launch_bounds__(kFinishThreads) void final_kernel(const Args a) {
     __syncthreads();
   }
   auto entry = [&](unsigned int j) { return staged ? s_keys[j] : global_entry(j); };
-  for (int pass = 2; pass < 5; ++pass) {
-    for (int b = threadIdx.x; b < kBins; b += kFinishThreads) s_tot[b] = 0u;
-    __syncthreads();
-    const int sh = digit_shift(pass - 1);
-    const unsigned long long want = s_prefix >> sh;
+  if (total <= unsigned(kFinishThreads)) {
+    // A short list 2 (the usual case) is ranked directly: keys are distinct (each holds its
+    // flat index), and a key is at or above k* exactly when fewer than k_rem keys of list 2
+    // are larger, k_rem being k*'s rank among them. Every thread reads every key (LDS
+    // broadcast) and counts those above its own.
+    const unsigned long long k_rem = s_k;
+    if (threadIdx.x < total) {
+      const unsigned long long mine = s_keys[threadIdx.x];
+      unsigned int above = 0;
+      for (unsigned int j = 0; j < total; ++j) above += s_keys[j] > mine ? 1u : 0u;
+      if (above < k_rem) a.keep[~static_cast<uint32_t>(mine)] = 1u;
+    }
+  } else {
+    for (int pass = 2; pass < 5; ++pass) {
+      for (int b = threadIdx.x; b < kBins; b += kFinishThreads) s_tot[b] = 0u;
+      __syncthreads();
+      const int sh = digit_shift(pass - 1);
+      const unsigned long long want = s_prefix >> sh;
+      for (unsigned int j = threadIdx.x; j < total; j += kFinishThreads) {
+        const unsigned long long key = entry(j);
+        if ((key >> sh) == want) atomicAdd(&s_tot[digit_of(key, pass)], 1u);
+      }
+      __syncthreads();
+      select_digit<kFinishThreads>(s_tot, pass, &s_prefix, &s_k);
+    }
+    const unsigned long long kstar = s_prefix;
     for (unsigned int j = threadIdx.x; j < total; j += kFinishThreads) {
       const unsigned long long key = entry(j);
-      if ((key >> sh) == want) atomicAdd(&s_tot[digit_of(key, pass)], 1u);
+      if (key >= kstar) a.keep[~static_cast<uint32_t>(key)] = 1u;
     }
-    __syncthreads();
-    select_digit<kFinishThreads>(s_tot, pass, &s_prefix, &s_k);
-  }
-  const unsigned long long kstar = s_prefix;
-  for (unsigned int j = threadIdx.x; j < total; j += kFinishThreads) {
-    const unsigned long long key = entry(j);
-    if (key >= kstar) a.keep[~static_cast<uint32_t>(key)] = 1u;
   }
   // Rule 1: every row's current position stays (pass 1 gave it the value of its top digit).
   const int64_t rows = a.n / a.N;
