@@ -46,7 +46,7 @@ typedef struct kv_evict_params {
 
 /*
  * Workspace bytes kv_evict_select needs for `p`: 0 when the budget alone decides the result
- * (M - L*H <= 0, or M - L*H >= L*H*(N - 1)), otherwise 397568 bytes of selection state and
+ * (M - L*H <= 0, or M - L*H >= L*H*(N - 1)), otherwise 495872 bytes of selection state and
  * histograms plus two candidate lists of 8 bytes per slot, each with at least L*H*N slots
  * (rounded up to whole blocks of 16384 entries per workgroup). Returns 0 for invalid `p`.
  */

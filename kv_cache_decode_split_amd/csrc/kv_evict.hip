@@ -65,14 +65,21 @@ constexpr int kListGrid = 64;                        // workgroups of the list p
 constexpr int kFinishThreads = 1024;                 // list-pass and final workgroups
 constexpr int kLdsKeys = 6144;                       // list-2 entries the final kernel stages
 constexpr int kBins = 8192;                          // 13-bit digits
+constexpr int kGroups = 64;                          // coarse bins: 128 consecutive digits each
+constexpr int kGroupBins = kBins / kGroups;
+// Group counters sit one 128-byte line apart: device-scope atomics from many workgroups to words
+// of one line serialise (packed, the 64 counters of a replica made pass 1 2.2x slower on MI355X).
+constexpr int kGroupStride = 32;
+constexpr int kRep = kBins + kGroups * kGroupStride; // words per replica: bins, then groups
 constexpr int kReplicas0 = KV_EVICT_REPLICAS;        // copies of the top digit's histogram
 constexpr int kReplicas1 = 4;                        // copies of the second digit's histogram
 constexpr size_t kStateBytes = 256;
-constexpr size_t kHistBytes = size_t(kReplicas0 + kReplicas1) * kBins * 4;
+constexpr size_t kHistBytes = size_t(kReplicas0 + kReplicas1) * kRep * 4;
 constexpr size_t kCountBytes = 4096;                 // per-region list-1 and list-2 counts
 constexpr size_t kFixedBytes = kStateBytes + kHistBytes + kCountBytes;
 static_assert((kGrid + kListGrid) * 4 <= int(kCountBytes), "per-region counts");
 static_assert(kBins % kStreamThreads == 0 && kBins % kFinishThreads == 0, "bins per thread");
+static_assert(kGroupBins == 2 * 64 && (kRep * 4) % 16 == 0, "a wave reads a group's bins in pairs");
 
 __host__ __device__ constexpr int digit_shift(int pass) { return pass < 4 ? 51 - 13 * pass : 0; }
 __host__ __device__ constexpr int digit_bits(int pass) { return pass < 4 ? 13 : 12; }
@@ -97,8 +104,8 @@ struct Args {
   const float* scores;
   uint8_t* keep;
   State* st;
-  unsigned int* hist0;           // [kReplicas0][kBins]: top digit over the pool
-  unsigned int* hist1;           // [kReplicas1][kBins]: second digit over list 1
+  unsigned int* hist0;           // [kReplicas0][kRep]: top digit over the pool (bins, groups)
+  unsigned int* hist1;           // [kReplicas1][kRep]: second digit over list 1
   unsigned int* count1;          // [grid]: list-1 entries in each region
   unsigned int* count2;          // [list_grid]: list-2 entries in each region
   unsigned long long* list1;     // [grid][cap1]
@@ -174,32 +181,87 @@ __device__ __forceinline__ bool is_current(const Args& a, int64_t i) {
   return i - int64_t(row_of(a, i)) * a.N == a.current;
 }
 
-// Add a workgroup's LDS histogram into one replica of a global histogram (bins that stayed zero
-// are skipped, so a workgroup touches only the bins its entries fell into).
+// Add a workgroup's LDS histogram into one replica of a global histogram, bins and groups (bins
+// and groups that stayed zero are skipped, so a workgroup touches only what its entries hit).
+// Group sums: 16 consecutive lanes add 8 bins each and combine by shuffles.
 template <int THREADS>
 __device__ __forceinline__ void flush_hist(const unsigned int* h_lds, unsigned int* h_glob) {
+  static_assert(THREADS % 64 == 0 && (kGroups * 16) % THREADS == 0, "whole waves per pass");
   for (int i = threadIdx.x; i < kBins; i += THREADS) {
     const unsigned int c = h_lds[i];
     if (c != 0u) __hip_atomic_fetch_add(h_glob + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  for (int t = threadIdx.x; t < kGroups * 16; t += THREADS) {
+    const int grp = t >> 4;
+    const unsigned int* b = h_lds + grp * kGroupBins + (t & 15) * 8;
+    unsigned int c = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c += b[j];
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) c += __shfl_xor(c, off, 16);
+    if ((t & 15) == 0 && c != 0u)
+      __hip_atomic_fetch_add(h_glob + kBins + grp * kGroupStride, c, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-// s_tot[b] = sum over the R replicas of bin b, with every load issued before any is used.
-template <int R, int THREADS>
-__device__ __forceinline__ void sum_replicas(const unsigned int* h, unsigned int* s_tot) {
-  constexpr int PER = kBins / THREADS;
-  unsigned int v[PER][R];
+// Fixes digit `pass` of k* from a global histogram of R replicas (bins and groups of 128 bins):
+// the bin, scanned from the top, in which the running count first reaches *k_rem. Wave 0 alone
+// reads the 64 group totals (one per lane), finds the group, then reads that group's 128 bins
+// (two per lane, the top ones in lane 0) and finds the bin; the other waves wait at the
+// barrier. Updates *prefix and *k_rem (LDS) for the whole workgroup.
+template <int R>
+__device__ void select_digit_global(const unsigned int* h, int pass, unsigned long long* prefix,
+                                    unsigned long long* k_rem) {
+  if (threadIdx.x < 64) {
+    const int lane = int(threadIdx.x);
+    unsigned int v[R];
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
+    for (int r = 0; r < R; ++r) v[r] = h[size_t(r) * kRep + kBins + lane * kGroupStride];
+    unsigned int c = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) v[j][r] = h[size_t(r) * kBins + j * THREADS + threadIdx.x];
+    for (int r = 0; r < R; ++r) c += v[r];
+    // Counts above this lane's group: a suffix sum over the lanes.
+    unsigned int suf = c;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    unsigned int t = 0;
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int y = __shfl_down(suf, off);
+      if (lane + off < 64) suf += y;
+    }
+    const unsigned long long k = *k_rem;
+    const unsigned long long above = suf - c;
+    const unsigned long long hit = __ballot(above < k && k <= above + c);
+    const int grp = hit != 0ull ? __ffsll(static_cast<long long>(hit)) - 1 : 0;
+    const unsigned long long k1 = k - static_cast<unsigned long long>(__shfl(suf - c, grp));
+    // Lane l holds bins top - 2l and top - 2l - 1 of the group.
+    const int bin_a = grp * kGroupBins + kGroupBins - 1 - 2 * lane;
+    unsigned int fa = 0, fb = 0;
+    unsigned int wa[R], wb[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) t += v[j][r];
-    s_tot[j * THREADS + threadIdx.x] = t;
+    for (int r = 0; r < R; ++r) {
+      wa[r] = h[size_t(r) * kRep + bin_a];
+      wb[r] = h[size_t(r) * kRep + bin_a - 1];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      fa += wa[r];
+      fb += wb[r];
+    }
+    const unsigned int local = fa + fb;
+    unsigned int inc = local;  // counts of this lane's bins and every higher one in the group
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    const unsigned long long before = inc - local;
+    if (hit != 0ull && before < k1 && k1 <= before + local) {
+      const bool top = k1 <= before + fa;
+      *prefix |= static_cast<unsigned long long>(top ? bin_a : bin_a - 1) << digit_shift(pass);
+      *k_rem = top ? k1 - before : k1 - before - fa;
+    }
   }
+  __syncthreads();
 }
 
 // Exclusive prefix sum over the workgroup's threads in thread order (s_wave: THREADS/64 words).
@@ -252,8 +314,9 @@ __device__ void select_digit(const unsigned int* s_tot, int pass, unsigned long 
 }
 
 // Clears the histograms. The passes histogram every entry, current positions included; to leave
-// the pool's histogram, workgroup 0 starts replica 0 of the top-digit histogram at minus the
-// current positions' counts (unsigned wrap-around cancels exactly once they are added).
+// the pool's histogram, workgroup 0 starts replica 0 of the top-digit histogram (bins and
+// groups) at minus the current positions' counts (unsigned wrap-around cancels exactly once
+// they are added).
 __global__ __launch_bounds__(256) void init_kernel(const Args a) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   __shared__ unsigned int h[kBins];
@@ -265,11 +328,16 @@ __global__ __launch_bounds__(256) void init_kernel(const Args a) {
       atomicAdd(&h[top_digit(a.scores[r * a.row_stride + a.current])], 1u);
     __syncthreads();
     for (int i = threadIdx.x; i < kBins; i += 256) a.hist0[i] = 0u - h[i];
+    if (threadIdx.x < kGroups) {
+      unsigned int c = 0;
+      for (int j = 0; j < kGroupBins; ++j) c += h[threadIdx.x * kGroupBins + j];
+      a.hist0[kBins + threadIdx.x * kGroupStride] = 0u - c;
+    }
     return;
   }
   const int i = int(blockIdx.x - 1) * 256 + int(threadIdx.x);  // one 16-byte piece past replica 0
-  constexpr int kPieces = (kReplicas0 + kReplicas1 - 1) * kBins / 4;
-  if (i < kPieces) reinterpret_cast<u32x4_t*>(a.hist0 + kBins)[i] = u32x4_t{0u, 0u, 0u, 0u};
+  constexpr int kPieces = (kReplicas0 + kReplicas1 - 1) * kRep / 4;
+  if (i < kPieces) reinterpret_cast<u32x4_t*>(a.hist0 + kRep)[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
 // Pass 0: histogram of the top digit over the whole pool.
@@ -292,7 +360,7 @@ __global__ __launch_bounds__(kStreamThreads) void pass0_kernel(const Args a) {
     }
   }
   __syncthreads();
-  flush_hist<kStreamThreads>(h, a.hist0 + size_t(blockIdx.x % kReplicas0) * kBins);
+  flush_hist<kStreamThreads>(h, a.hist0 + size_t(blockIdx.x % kReplicas0) * kRep);
 }
 
 // Pass 1: fixes k*'s top digit (every workgroup, identically), then the whole mask, list 1 in
@@ -302,21 +370,19 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(const Args a) {
   __shared__ unsigned int h[kBins];
   __shared__ unsigned long long s_prefix, s_k;
   __shared__ unsigned int s_n;
-  sum_replicas<kReplicas0, kStreamThreads>(a.hist0, h);
+  for (int i = threadIdx.x; i < kBins; i += kStreamThreads) h[i] = 0u;
   if (threadIdx.x == 0) {
     s_prefix = 0ull;
     s_k = a.k;
     s_n = 0u;
   }
   __syncthreads();
-  select_digit<kStreamThreads>(h, 0, &s_prefix, &s_k);
+  select_digit_global<kReplicas0>(a.hist0, 0, &s_prefix, &s_k);
   const int d0 = digit_of(s_prefix, 0);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.st->prefix0 = s_prefix;
     a.st->k_rem0 = s_k;
   }
-  for (int i = threadIdx.x; i < kBins; i += kStreamThreads) h[i] = 0u;
-  __syncthreads();
   unsigned long long* region = a.list1 + int64_t(blockIdx.x) * a.cap1;
   for (int64_t base = int64_t(blockIdx.x) * kChunk; base < a.n; base += int64_t(gridDim.x) * kChunk) {
     float x[kSlabs][4];
@@ -352,24 +418,22 @@ __global__ __launch_bounds__(kStreamThreads) void pass1_kernel(const Args a) {
   }
   __syncthreads();
   if (threadIdx.x == 0) a.count1[blockIdx.x] = s_n;
-  flush_hist<kStreamThreads>(h, a.hist1 + size_t(blockIdx.x % kReplicas1) * kBins);
+  flush_hist<kStreamThreads>(h, a.hist1 + size_t(blockIdx.x % kReplicas1) * kRep);
 }
 
 // List pass: every workgroup fixes k*'s second digit (identically), then walks the list-1
 // regions r = blockIdx.x, blockIdx.x + gridDim.x, ...: entries above k*'s first two digits get
 // a 1, entries sharing them go to this workgroup's list-2 region.
 __global__ __launch_bounds__(kFinishThreads) void list_kernel(const Args a) {
-  __shared__ unsigned int s_tot[kBins];
   __shared__ unsigned long long s_prefix, s_k;
   __shared__ unsigned int s_n;
-  sum_replicas<kReplicas1, kFinishThreads>(a.hist1, s_tot);
   if (threadIdx.x == 0) {
     s_prefix = a.st->prefix0;
     s_k = a.st->k_rem0;
     s_n = 0u;
   }
   __syncthreads();
-  select_digit<kFinishThreads>(s_tot, 1, &s_prefix, &s_k);
+  select_digit_global<kReplicas1>(a.hist1, 1, &s_prefix, &s_k);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.st->prefix1 = s_prefix;
     a.st->k_rem1 = s_k;
@@ -579,7 +643,7 @@ kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept
     char* ws = static_cast<char*>(workspace);
     a.st = reinterpret_cast<State*>(ws);
     a.hist0 = reinterpret_cast<unsigned int*>(ws + kStateBytes);
-    a.hist1 = a.hist0 + size_t(kReplicas0) * kBins;
+    a.hist1 = a.hist0 + size_t(kReplicas0) * kRep;
     a.count1 = reinterpret_cast<unsigned int*>(ws + kStateBytes + kHistBytes);
     a.count2 = a.count1 + kGrid;
     a.list1 = reinterpret_cast<unsigned long long*>(ws + kFixedBytes);
@@ -597,7 +661,7 @@ kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept
     const bool vec = p->row_stride == p->num_tokens && a.n % 4 == 0 && aligned(scores, 16) &&
                      aligned(keep, 4);
     hipLaunchKernelGGL(init_kernel,
-                       dim3(1 + ((kReplicas0 + kReplicas1 - 1) * kBins / 4 + 255) / 256), dim3(256),
+                       dim3(1 + ((kReplicas0 + kReplicas1 - 1) * kRep / 4 + 255) / 256), dim3(256),
                        0, s, a);
     if (vec) {
       hipLaunchKernelGGL(pass0_kernel<true>, dim3(g.grid), dim3(kStreamThreads), 0, s, a);
