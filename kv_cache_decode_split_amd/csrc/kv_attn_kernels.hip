@@ -185,7 +185,8 @@ __device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
 #endif
 
 // PAGED: 0 contiguous, 1 paged, 2 decided at run time.
-// R = 0: one query token per sequence (G = compiled group width). R > 0 ("rows" mode, variant 2):
+// R = 0: one query token per sequence (G = compiled group width). R > 0 ("rows" mode, variant 2:
+// several query tokens per sequence, or one token with a bf16 group of 4 or more heads):
 // num_queries tokens per sequence, the group's query rows (token-major, then head) packed into R
 // blocks of 16 MFMA columns; scores and P.V both on the matrix cores (G unused).
 // SCORES: score export (one query token): every visited position's base-2 score goes to
