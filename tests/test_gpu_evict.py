@@ -170,3 +170,35 @@ def test_full_size_selections(name):
         assert np.array_equal(got, _oracle(scores, budget, N - 1))
     del scores, keep
     torch.cuda.empty_cache()
+
+
+def test_selection_over_a_billion_entries():
+    """2^30 entries (16 layers x 16 heads x 4,194,304 positions; flat indices up to 2^30 in the
+    keys, 16 GiB of candidate lists): checked on the GPU by the properties that fix the set
+    (kept count, every kept pool score at least every dropped one, ties kept in index order)."""
+    E = _evict()
+    L, H, N = 16, 16, 1 << 22
+    budget = L * H + (L * H * (N - 1)) // 7
+    announce(f"evict 2^30 entries M={budget}")
+    scores = W.make_scores(L, H, N, "lognormal", seed=2099, device="cuda")
+    counts = torch.empty((L, H), dtype=torch.int32, device="cuda")
+    keep = E.kv_evict_select(scores, budget, kept_per_row=counts).bool()
+    try:
+        assert keep[:, :, N - 1].all()
+        assert torch.equal(counts, keep.sum(dim=2, dtype=torch.int32))
+        pool_kept = keep.clone()
+        pool_kept[:, :, N - 1] = False
+        assert int(pool_kept.sum()) == budget - L * H
+        inf = torch.tensor(float("inf"), device="cuda")
+        lo = torch.where(pool_kept, scores, inf).min()
+        hi = torch.where(keep, -inf, scores).max()
+        assert float(lo) >= float(hi)
+        if float(lo) == float(hi):
+            flat = torch.arange(L * H * N, device="cuda").view(L, H, N)
+            big = torch.tensor(L * H * N, device="cuda")
+            last_kept = torch.where(pool_kept & (scores == lo), flat, -1).max()
+            first_dropped = torch.where(~keep & (scores == lo), flat, big).min()
+            assert int(last_kept) < int(first_dropped)
+    finally:
+        del scores, keep
+        torch.cuda.empty_cache()
