@@ -320,19 +320,21 @@ __device__ void select_digit(const unsigned int* s_tot, int pass, unsigned long 
 __global__ __launch_bounds__(256) void init_kernel(const Args a) {
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   __shared__ unsigned int h[kBins];
+  __shared__ unsigned int hg[kGroups];
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0u;
+    if (threadIdx.x < kGroups) hg[threadIdx.x] = 0u;
     __syncthreads();
     const int64_t rows = a.n / a.N;
-    for (int64_t r = threadIdx.x; r < rows; r += 256)
-      atomicAdd(&h[top_digit(a.scores[r * a.row_stride + a.current])], 1u);
+    for (int64_t r = threadIdx.x; r < rows; r += 256) {
+      const int d = top_digit(a.scores[r * a.row_stride + a.current]);
+      atomicAdd(&h[d], 1u);
+      atomicAdd(&hg[d / kGroupBins], 1u);  // group totals counted directly: summing 128
+                                            // LDS words a thread would conflict on one bank
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < kBins; i += 256) a.hist0[i] = 0u - h[i];
-    if (threadIdx.x < kGroups) {
-      unsigned int c = 0;
-      for (int j = 0; j < kGroupBins; ++j) c += h[threadIdx.x * kGroupBins + j];
-      a.hist0[kBins + threadIdx.x * kGroupStride] = 0u - c;
-    }
+    if (threadIdx.x < kGroups) a.hist0[kBins + threadIdx.x * kGroupStride] = 0u - hg[threadIdx.x];
     return;
   }
   const int i = int(blockIdx.x - 1) * 256 + int(threadIdx.x);  // one 16-byte piece past replica 0
