@@ -153,8 +153,9 @@ const char* kv_attn_status_string(int32_t status);
  * current HIP device). Validates `p` exactly as kv_attn_decode does (pointers aside). Split
  * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
  * workgroups number at least about one per compute unit (two for kernel_variant 2 with more
- * than 16 query rows per KV head), each split spans at least 16 tiles and at most 256 (512 when
- * batch * num_kv_heads is under half the compute units, or with num_queries > 1), and a
+ * than 16 query rows per KV head), there are at most ceil(tiles / 16) splits, each spans at most
+ * 256 tiles (512 when batch * num_kv_heads is under half the compute units, or with
+ * num_queries > 1), and a
  * caller-given num_splits overrides the count. With a window the tiles counted are those a
  * sequence can visit: ceil(min(num_sinks, max_ctx_len) / 16) + ceil((window + gamma - 1) / 16)
  * + 1 at most, gamma being num_queries (the union of the gamma query tokens' windows).

@@ -10,6 +10,7 @@ import re
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 import torch
 
@@ -189,6 +190,42 @@ def test_plan_covers_every_tile_and_respects_bounds():
             # at most 256 tiles per split with many (sequence, KV head) units, 512 with few
             cap = 512 if B * hkv * 2 < cus else 256
             assert L // 16 <= cap or S == 4096
+
+
+def test_random_plans_cover_the_visited_tiles_within_the_bounds():
+    """Seeded sweep over shapes, windows, query tokens and CU counts: the splits cover exactly
+    the tiles a sequence can visit, within the split-length bounds, and the workspace holds
+    every split state."""
+    rnd = np.random.default_rng(17)
+    for _ in range(400):
+        B = int(rnd.integers(1, 200))
+        hkv = int(rnd.choice([1, 2, 4, 8, 32]))
+        g = int(rnd.choice([1, 2, 3, 4, 8, 16]))
+        nq = int(rnd.choice([1, 1, 2, 4]))
+        if nq * g > 32:
+            nq = 1
+        T = int(rnd.choice([1, 15, 16, 17, 300, 4096, 8191, 32768, 131072, 1 << 20]))
+        W = int(rnd.choice([0, 0, 1, 64, 1000, 4096]))
+        n = int(rnd.choice([0, 4, 100]))
+        cus = int(rnd.choice([1, 64, 256, 304]))
+        p = _params(batch=B, num_q_heads=hkv * g, num_kv_heads=hkv, max_ctx_len=T,
+                    max_blocks_per_seq=(T + 15) // 16, num_blocks=10**7, window=W or None, num_sinks=n,
+                    num_queries=nq)
+        plan = K.kv_attn_get_plan(p, cus)
+        all_tiles = (T + 15) // 16
+        bound = all_tiles if W == 0 else min(all_tiles, (min(n, T) + 15) // 16
+                                              + (W + nq - 1 + 15) // 16 + 1)
+        S, L = plan["num_splits"], plan["split_len"]
+        label = (B, hkv, g, nq, T, W, n, cus, S, L)
+        assert L % 16 == 0 and 1 <= S <= 4096, label
+        assert S * (L // 16) >= bound and (S - 1) * (L // 16) < bound, label
+        assert L // 16 <= 512 or S == 4096, label
+        if S > 1:
+            assert S <= -(-bound // 16), label   # at most one split per 16 visited tiles
+            rows = B * nq * hkv * g
+            assert plan["grid_merge"] == rows
+            assert plan["workspace_bytes"] >= rows * S * (128 + 2) * 4, label
+        assert plan["grid_split"] == B * hkv * S, label
 
 
 def test_plan_for_the_five_workloads():
