@@ -128,14 +128,15 @@ typedef struct kv_attn_params {
 typedef struct kv_attn_plan {
   int32_t num_splits;       /* S: splits per (sequence, KV head) */
   int32_t split_len;        /* positions per split, a multiple of 16 */
-  int32_t grid_split;       /* workgroups of the split kernel: batch * num_kv_heads * S */
+  int32_t grid_split;       /* workgroups of the split kernel: batch * num_kv_heads * S (times 2
+                               when kernel_variant 0 serves a group above 8 heads in halves) */
   int32_t grid_merge;       /* workgroups of the merge kernel: batch * num_queries *
                                num_q_heads (0 when S == 1) */
   int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores,
                                2: bf16 MFMA scores and P.V ("rows mode": num_queries > 1, or
                                one token with a group of 4 or more query heads per KV head;
                                kv_attn_decode_scores runs variant 1 in its place) */
-  int32_t group_padded;     /* compiled group width (power of two >= g) */
+  int32_t group_padded;     /* compiled group width (power of two >= g; 8 for the halves above) */
   int32_t num_cus;          /* compute units the plan was made for */
   int32_t reserved;
   uint64_t workspace_bytes; /* workspace kv_attn_decode needs (0 when S == 1) */

@@ -257,6 +257,7 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.window = p->window;
     a.num_sinks = p->num_sinks;
     a.num_queries = plan.num_queries;
+    a.head_chunks = plan.head_chunks;
     a.logits = logits;
     a.logits_ld = sl.ld;
     a.row_stats = plan.num_splits == 1 ? row_stats : nullptr;

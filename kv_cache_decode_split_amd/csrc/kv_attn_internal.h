@@ -26,6 +26,7 @@ constexpr int kMaxSplits = 4096;
 constexpr int kMaxQueryRows = 32;      // rows mode: num_queries * group <= 32 (two MFMA blocks)
 constexpr int kMaxQueries = 16;
 constexpr int kRowsMinGroup = 4;      // one query token: rows mode from this group size on (bf16)
+constexpr int kVectorMaxGroup = 8;    // vector path: query heads one workgroup holds
 
 // Everything the split kernel needs, by value.
 struct SplitArgs {
@@ -51,6 +52,8 @@ struct SplitArgs {
   int32_t window;              // > 0: attend only the last `window` positions plus the sinks
   int32_t num_sinks;           // leading positions always attended when a window is set
   int32_t num_queries;         // query tokens per sequence (rows mode; 1 otherwise)
+  int32_t head_chunks;         // workgroups per (sequence, KV head, split): 1, or 2 when the
+                               // vector path serves a group above kVectorMaxGroup heads
   float* logits;               // nullptr, or [B * h_q, logits_ld]: base-2 scores of every visited
                                // position (one query token per sequence only)
   int64_t logits_ld;           // multiple of kTile, >= max_ctx rounded up to kTile
@@ -122,6 +125,7 @@ struct Plan {
   int32_t variant;  // 0: vector fp32 path, 1: MFMA scores, 2: MFMA scores and P.V (rows mode)
   int32_t num_queries;  // query tokens per sequence (>= 1)
   int32_t row_blocks;   // rows mode: blocks of 16 query rows per (sequence, KV head)
+  int32_t head_chunks;  // vector path: the group's query heads served by this many workgroups
   int64_t grid_split;
   int64_t grid_merge;
   uint64_t workspace_bytes;

@@ -228,9 +228,15 @@ void split_kernel(const SplitArgs a) {
   const int units = int(gridDim.x) / S;
   const int split = blockIdx.x / units;
   const int unit = blockIdx.x - split * units;
-  const int b = unit / a.h_kv;
-  const int kvh = (unit - b * a.h_kv + split) % a.h_kv;
-  const int g = a.group;
+  // With head chunks (vector path, groups above G heads) consecutive units are the chunks of one
+  // (sequence, KV head): chunk hc serves query heads h0 .. h0 + g - 1 of the group.
+  const int hcn = a.head_chunks;
+  const int hc = unit % hcn;
+  const int unit_kv = unit / hcn;
+  const int b = unit_kv / a.h_kv;
+  const int kvh = (unit_kv - b * a.h_kv + split) % a.h_kv;
+  const int h0 = hc * G;
+  const int g = hcn > 1 ? min(G, a.group - h0) : a.group;  // query heads this workgroup serves
   const bool paged = PAGED == 2 ? (a.block_table != nullptr) : (PAGED == 1);
 
   int ctx = a.ctx_lens[b];
@@ -256,7 +262,7 @@ void split_kernel(const SplitArgs a) {
     if constexpr (ROWS)
       return (int64_t(b) * nq + rho / g) * a.h_q + int64_t(kvh) * g + rho % g;
     else
-      return int64_t(b) * a.h_q + int64_t(kvh) * g + rho;
+      return int64_t(b) * a.h_q + int64_t(kvh) * a.group + h0 + rho;
   };
   if (t_begin >= ntiles) {
     // Only an empty sequence reaches here with one split: its rows are defined as zeros.
@@ -452,7 +458,7 @@ void split_kernel(const SplitArgs a) {
   // the path that takes them. (a.logits is null outside the score-export instantiations; the
   // descriptor is then unused.)
   const __amdgpu_buffer_rsrc_t score_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      SCORES ? a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * g) * a.logits_ld : a.logits, 0,
+      SCORES ? a.logits + (int64_t(b) * a.h_q + int64_t(kvh) * a.group + h0) * a.logits_ld : a.logits, 0,
       SCORES ? int(a.logits_ld * g * 4) : 0, kBufferRsrcWord3);
   auto store_scores = [&](f32x4_t v, int pos, int j) __attribute__((always_inline)) {
     const uint32_t off = j < g ? uint32_t((int64_t(j) * a.logits_ld + pos) * 4) : 0x80000000u;
@@ -956,7 +962,10 @@ int launch_scores_variant(const SplitArgs& a, const Plan& plan, bool paged, bool
   if (plan.variant == 1)
     return paged ? launch_one<D, G, true, true, true, 1, 0, true>(a, plan.grid_split, s)
                  : launch_one<D, G, true, true, true, 0, 0, true>(a, plan.grid_split, s);
-  if (!q_bf16 && !kv_bf16) return launch_one<D, G, false, false, false, 2, 0, true>(a, plan.grid_split, s);
+  if constexpr (G <= kVectorMaxGroup) {
+    if (!q_bf16 && !kv_bf16)
+      return launch_one<D, G, false, false, false, 2, 0, true>(a, plan.grid_split, s);
+  }
   return int(hipErrorInvalidValue);
 }
 
@@ -980,10 +989,14 @@ int launch_dtype(const SplitArgs& a, const Plan& plan, bool paged, bool q_bf16, 
     return paged ? launch_one<D, G, true, true, true, 1>(a, plan.grid_split, s)
                  : launch_one<D, G, true, true, true, 0>(a, plan.grid_split, s);
   }
-  if (q_bf16 && kv_bf16) return launch_one<D, G, true, true, false, 2>(a, plan.grid_split, s);
-  if (q_bf16) return launch_one<D, G, true, false, false, 2>(a, plan.grid_split, s);
-  if (kv_bf16) return launch_one<D, G, false, true, false, 2>(a, plan.grid_split, s);
-  return launch_one<D, G, false, false, false, 2>(a, plan.grid_split, s);
+  if constexpr (G <= kVectorMaxGroup) {
+    if (q_bf16 && kv_bf16) return launch_one<D, G, true, true, false, 2>(a, plan.grid_split, s);
+    if (q_bf16) return launch_one<D, G, true, false, false, 2>(a, plan.grid_split, s);
+    if (kv_bf16) return launch_one<D, G, false, true, false, 2>(a, plan.grid_split, s);
+    return launch_one<D, G, false, false, false, 2>(a, plan.grid_split, s);
+  } else {
+    return int(hipErrorInvalidValue);  // the planner serves larger groups in head chunks
+  }
 }
 
 template <int D>

@@ -119,6 +119,7 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   const bool bf16 = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && !force_vector;
   plan->num_queries = nq;
   plan->row_blocks = 0;
+  plan->head_chunks = 1;
   // Rows mode (variant 2) also serves one token once the group has kRowsMinGroup heads: P.V
   // then costs less on the matrix cores than as per-lane FMAs for every head (on MI355X the
   // C5 shape, group 8, went from 0.79 to 0.82 of peak, at the bandwidth of the loads alone).
@@ -128,6 +129,11 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   } else {
     plan->variant = bf16 ? 1 : 0;
   }
+  // The vector path (fp32 or mixed inputs) holds every head's query and output slices in
+  // registers; above kVectorMaxGroup heads that spilled hundreds of registers to scratch, so
+  // two workgroups then serve the halves of the group (each reading the KV head once).
+  if (plan->variant == 0 && g > kVectorMaxGroup) plan->head_chunks = 2;
+  const int64_t work_units = units * plan->head_chunks;
 
   int64_t S;
   if (p->num_splits > 0) {
@@ -136,13 +142,13 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
     // About one split workgroup per CU; two for two-block rows mode, which keeps one tile in
     // flight per wave and needs two waves per SIMD to keep enough loads outstanding.
     const int64_t per_cu = plan->row_blocks == 2 ? 2 : 1;
-    S = ceil_div(int64_t(num_cus) * per_cu, units);
+    S = ceil_div(int64_t(num_cus) * per_cu, work_units);
     // Split length cap: 256 tiles keep a batch of many (sequence, KV head) units balanced when
     // its lengths are ragged; with few units (long sequences split for parallelism) or several
     // query tokens (heavier per-split epilogue and merge rows) 512 tiles stream faster. MI355X
     // sweeps: C4 (1024 units, ragged) best at 256; C5 (32 units) 0.825 at 512 against 0.815;
     // C3 with 8 tokens 0.828 against 0.776, C5 with 4 tokens 0.807 against 0.755.
-    const int64_t cap = (nq > 1 || units * 2 < num_cus) ? kMaxSplitTilesLong : kMaxSplitTiles;
+    const int64_t cap = (nq > 1 || work_units * 2 < num_cus) ? kMaxSplitTilesLong : kMaxSplitTiles;
     const int64_t most = ceil_div(tiles_max, kMinSplitTiles);  // splits of >= 16 tiles
     const int64_t least = ceil_div(tiles_max, cap);
     if (S > most) S = most;
@@ -156,8 +162,8 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
 
   plan->num_splits = int32_t(S);
   plan->split_tiles = int32_t(split_tiles);
-  plan->group_padded = padded_group(g);
-  plan->grid_split = units * S;
+  plan->group_padded = plan->head_chunks > 1 ? kVectorMaxGroup : padded_group(g);
+  plan->grid_split = work_units * S;
   const int64_t rows = int64_t(p->batch) * nq * p->num_q_heads;
   plan->grid_merge = S > 1 ? rows : 0;
   if (S > 1) {

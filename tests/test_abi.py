@@ -259,6 +259,12 @@ def test_explicit_split_count_and_variant_selection():
         assert K.kv_attn_get_plan(_params(num_q_heads=8 * g), 256)["kernel_variant"] == 2, g
     p = _params(num_q_heads=8 * 8, q_dtype=K.KV_ATTN_F32, kv_dtype=K.KV_ATTN_F32)
     assert K.kv_attn_get_plan(p, 256)["kernel_variant"] == 0
+    # the vector path serves a group above 8 heads with two workgroups of up to 8 heads each
+    for g in (9, 16):
+        for qd, kd in ((K.KV_ATTN_F32, K.KV_ATTN_F32), (K.KV_ATTN_BF16, K.KV_ATTN_F32)):
+            plan = K.kv_attn_get_plan(_params(num_q_heads=8 * g, q_dtype=qd, kv_dtype=kd), 256)
+            assert plan["kernel_variant"] == 0 and plan["group_padded"] == 8
+            assert plan["grid_split"] == 2 * 4 * 8 * plan["num_splits"]
 
 
 def _decode_raw(p, q=16, k=16, v=16, bt=16, ctx=16, out=16, ws=None, ws_bytes=0):

@@ -35,6 +35,9 @@ SMALL = [
     ("C4", dict(batch=5, ctx=("uniform", 1, 300), layout="token_major", extra_blocks=7)),
     ("C5", dict(batch=2, ctx=(3000, 2999))),
     ("C5", dict(batch=3, ctx=(3000, 1, 2999), block_order="sequential")),
+    # vector path above 8 heads per KV head: two workgroups serve the halves of the group
+    ("C1", dict(batch=2, ctx=(700, 333), head_dim=128, num_q_heads=32, num_kv_heads=2)),
+    ("C4", dict(batch=3, ctx=(900, 1, 450), num_q_heads=96, num_kv_heads=8, q_dtype="f32")),
     ("C4", dict(batch=6, ctx=("uniform", 1, 700), block_order="sequential", num_kv_heads=16,
                 num_q_heads=32)),
 ]

@@ -60,6 +60,7 @@ SMALL = [
     ("C5", dict(batch=2, ctx=(3000, 1777))),                               # g = 8, sinks
     ("C5", dict(batch=2, ctx=(900, 333), num_q_heads=16, num_kv_heads=1, head_dim=64)),  # g = 16
     ("C1", dict(batch=2, ctx=(256, 100), head_dim=128, num_q_heads=16, num_kv_heads=2)),
+    ("C1", dict(batch=2, ctx=(500, 90), head_dim=128, num_q_heads=32, num_kv_heads=2)),  # g = 16, halves
 ]
 
 
