@@ -789,11 +789,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 // M = max_s m_s, w_s = 2^(m_s - M) (0 for an empty state), out = sum_s w_s O_s / sum_s w_s l_s.
 // Threads first share the maxima and weights of all splits, then each output element is
 // accumulated over kMergeThreads / D interleaved subsets of splits (independent loads in flight)
-// and the subsets are added in a fixed order.
+// and the subsets are added in a fixed order. The loads that depend on nothing (the row's
+// length or valid count, the first split states and the first partial outputs) are all issued
+// before any is used, so a row costs one memory round trip instead of three; entries past the
+// valid count lie inside the workspace and are read but never used.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a) {
   constexpr int SUB = kMergeThreads / D;
   constexpr int NW = kMergeThreads / 64;
+  constexpr int PRE = 8;  // partial-output loads per thread issued up front
   __shared__ float s_w[kMaxSplits];
   __shared__ float s_red[NW];
   __shared__ float s_acc[SUB][D];
@@ -802,13 +806,34 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
   const int wave = tid >> 6;
   const int row = blockIdx.x;
   const int S = a.num_splits;
+  const float* ml = a.ml_part + int64_t(row) * S * 2;
+  const float* o = a.o_part + int64_t(row) * S * D;
+  const int e = tid % D;
+  const int sub = tid / D;
+
+  int raw = S;
+  if (a.num_valid != nullptr)
+    raw = a.num_valid[row];
+  else if (a.ctx_lens != nullptr)
+    raw = a.ctx_lens[row / a.h_q];
+  float m_first = neg_inf(), l_first = 0.f;
+  if (tid < S) {
+    m_first = ml[2 * tid];
+    l_first = ml[2 * tid + 1];
+  }
+  float o_pre[PRE];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int s = sub + k * SUB;
+    o_pre[k] = s < S ? o[int64_t(s) * D + e] : 0.f;
+  }
+
   int nv = S;
   if (a.num_valid != nullptr) {
-    nv = a.num_valid[row];
+    nv = raw;
   } else if (a.ctx_lens != nullptr) {
     // Same tile enumeration as the split kernel: splits past the sequence's tiles hold nothing.
-    int ctx = a.ctx_lens[row / a.h_q];
-    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+    const int ctx = raw < 0 ? 0 : (raw > a.max_ctx ? a.max_ctx : raw);
     int n_first = 0, win_tile0 = 0;
     if (a.window > 0) {
       n_first = (min(a.num_sinks, ctx) + kTile - 1) / kTile;
@@ -818,11 +843,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
     nv = (ntiles + a.split_tiles - 1) / a.split_tiles;
   }
   nv = nv < 0 ? 0 : (nv > S ? S : nv);
-  const float* ml = a.ml_part + int64_t(row) * S * 2;
-  const float* o = a.o_part + int64_t(row) * S * D;
 
-  float m_loc = neg_inf();
-  for (int s = tid; s < nv; s += kMergeThreads) m_loc = fmaxf(m_loc, ml[2 * s]);
+  float m_loc = tid < nv ? m_first : neg_inf();
+  for (int s = tid + kMergeThreads; s < nv; s += kMergeThreads) m_loc = fmaxf(m_loc, ml[2 * s]);
   m_loc = wave_max(m_loc);
   if (lane == 0) s_red[wave] = m_loc;
   __syncthreads();
@@ -833,10 +856,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
 
   float l_loc = 0.f;
   for (int s = tid; s < nv; s += kMergeThreads) {
-    const float m = ml[2 * s];
+    const float m = s == tid ? m_first : ml[2 * s];
+    const float l = s == tid ? l_first : ml[2 * s + 1];
     const float w = (m == neg_inf()) ? 0.f : exp2_fast(m - M);
     s_w[s] = w;
-    l_loc = fmaf(w, ml[2 * s + 1], l_loc);
+    l_loc = fmaf(w, l, l_loc);
   }
   l_loc = wave_sum(l_loc);
   if (lane == 0) s_red[wave] = l_loc;
@@ -845,10 +869,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const MergeArgs a)
 #pragma unroll
   for (int w = 0; w < NW; ++w) L += s_red[w];
 
-  const int e = tid % D;
-  const int sub = tid / D;
   float acc = 0.f;
-  int s = sub;
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int s = sub + k * SUB;
+    if (s < nv) acc = fmaf(s_w[s], o_pre[k], acc);
+  }
+  int s = sub + PRE * SUB;
   for (; s + 3 * SUB < nv; s += 4 * SUB) {
     const float o0 = o[int64_t(s) * D + e];
     const float o1 = o[int64_t(s + SUB) * D + e];
