@@ -98,6 +98,9 @@ def parse_args():
     ap.add_argument("--block-order", choices=["random", "sequential"], default=None,
                     help="paged workloads: deal the physical blocks to the sequences in a random "
                          "order (the workload's default) or in physical order")
+    ap.add_argument("--layout", choices=["head_major", "token_major"], default=None,
+                    help="cache layout: [.., KV head, position, d] (the workloads' default) or "
+                         "[.., position, KV head, d]")
     ap.add_argument("--scores", action="store_true",
                     help="each layer also exports the attention weight of every cached position "
                          "(kv_attn_decode_scores)")
@@ -155,6 +158,9 @@ def main():
         spec = dataclasses.replace(spec, block_order=args.block_order)
         if args.block_order != "random":
             tag = f"{tag}_{args.block_order}"
+    if args.layout is not None and args.layout != spec.layout:
+        spec = dataclasses.replace(spec, layout=args.layout)
+        tag = f"{tag}_{args.layout}"
     if args.gamma < 1:
         print("bench.py: --gamma must be >= 1", file=sys.stderr)
         sys.exit(2)
@@ -355,6 +361,7 @@ def main():
                 "(attention sinks), the rest NaN-poisoned and never read" if spec.window else "")
                 + ("; blocks dealt to the sequences in physical order"
                    if spec.paged and spec.block_order == "sequential" else "")
+                + ("; token-major cache layout" if spec.layout == "token_major" else "")
                 + (f"; {gamma} query tokens per sequence (speculative-decoding verification: the "
                    "last gamma cached positions, causal among themselves)" if gamma > 1 else ""),
             "num_queries": gamma,
@@ -367,7 +374,7 @@ def main():
             "block_order": spec.block_order if spec.paged else None,
             "unique_kv_bytes_per_step": kv_bytes_step, "flops_per_step": flops_step,
             "plan": {k: plan[k] for k in ("num_splits", "split_len", "grid_split", "grid_merge",
-                                          "kernel_variant", "num_cus")},
+                                          "kernel_variant", "wave_heads", "num_cus")},
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -129,7 +129,8 @@ typedef struct kv_attn_plan {
   int32_t num_splits;       /* S: splits per (sequence, KV head) */
   int32_t split_len;        /* positions per split, a multiple of 16 */
   int32_t grid_split;       /* workgroups of the split kernel: batch * num_kv_heads * S (times 2
-                               when kernel_variant 0 serves a group above 8 heads in halves) */
+                               when kernel_variant 0 serves a group above 8 heads in halves;
+                               divided by 4 with wave_heads) */
   int32_t grid_merge;       /* workgroups of the merge kernel: batch * num_queries *
                                num_q_heads (0 when S == 1) */
   int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores,
@@ -138,7 +139,20 @@ typedef struct kv_attn_plan {
                                kv_attn_decode_scores runs variant 1 in its place) */
   int32_t group_padded;     /* compiled group width (power of two >= g; 8 for the halves above) */
   int32_t num_cus;          /* compute units the plan was made for */
-  int32_t reserved;
+  int32_t wave_heads;       /* 1: each split workgroup serves 4 KV heads, one per wave, every
+                               wave streaming a whole split, so that a position's KV-head rows
+                               (token-major) or 4 adjacent head slices of a block (head-major)
+                               are read together. Needs num_kv_heads a multiple of 4 and no
+                               halves; chosen for token-major caches (both stride_head <
+                               stride_token) when batch * num_kv_heads < 4 * num_cus, and for
+                               other layouts when batch * num_kv_heads < num_cus / 2, there
+                               are at most 16 query rows per KV head and at least 1024 tiles
+                               (16384 positions); in both cases only when tiles *
+                               batch * num_kv_heads / 4 >= 32 * num_cus (64 * num_cus with 2
+                               row blocks), i.e. every wave gets >= 32 tiles on a full device.
+                               The automatic S then counts batch * num_kv_heads / 4 workgroups
+                               per split and allows one split per 4 tiles. 0: one KV head per
+                               workgroup. */
   uint64_t workspace_bytes; /* workspace kv_attn_decode needs (0 when S == 1) */
   uint64_t ml_offset;       /* byte offset of the (m, l) array inside the workspace (S > 1) */
 } kv_attn_plan;
@@ -154,9 +168,10 @@ const char* kv_attn_status_string(int32_t status);
  * current HIP device). Validates `p` exactly as kv_attn_decode does (pointers aside). Split
  * planning: tiles of 16 positions; the splits per sequence are chosen so that the split
  * workgroups number at least about one per compute unit (two for kernel_variant 2 with more
- * than 16 query rows per KV head), there are at most ceil(tiles / 16) splits, each spans at most
- * 256 tiles (512 when batch * num_kv_heads is under half the compute units, or with
- * num_queries > 1), and a
+ * than 16 query rows per KV head), there are at most ceil(tiles / 16) splits (ceil(tiles / 4)
+ * with wave_heads), each spans at most
+ * 256 tiles (512 when the split workgroups of one split are under half the compute units, or
+ * with num_queries > 1 or wave_heads), and a
  * caller-given num_splits overrides the count. With a window the tiles counted are those a
  * sequence can visit: ceil(min(num_sinks, max_ctx_len) / 16) + ceil((window + gamma - 1) / 16)
  * + 1 at most, gamma being num_queries (the union of the gamma query tokens' windows).

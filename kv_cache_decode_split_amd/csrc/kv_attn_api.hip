@@ -87,7 +87,7 @@ kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_att
   plan->kernel_variant = pl.variant;
   plan->group_padded = pl.group_padded;
   plan->num_cus = cus;
-  plan->reserved = 0;
+  plan->wave_heads = pl.wave_heads;
   plan->workspace_bytes = pl.workspace_bytes;
   plan->ml_offset = pl.num_splits > 1 ? pl.o_part_bytes : 0;
   return KV_ATTN_OK;
@@ -258,6 +258,7 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.num_sinks = p->num_sinks;
     a.num_queries = plan.num_queries;
     a.head_chunks = plan.head_chunks;
+    a.wave_heads = plan.wave_heads;
     a.logits = logits;
     a.logits_ld = sl.ld;
     a.row_stats = plan.num_splits == 1 ? row_stats : nullptr;

@@ -10,7 +10,8 @@ namespace kvattn {
 
 // Positions per tile: one MFMA row block, and one 16-token block of a paged cache.
 constexpr int kTile = 16;
-// Waves per split workgroup; each wave streams every kWaves-th tile of the split.
+// Waves per split workgroup; each wave streams every kWaves-th tile of the split (or, with
+// SplitArgs::wave_heads, every tile of the split for its own KV head).
 #ifndef KV_ATTN_WAVES
 #define KV_ATTN_WAVES 4
 #endif
@@ -27,6 +28,7 @@ constexpr int kMaxQueryRows = 32;      // rows mode: num_queries * group <= 32 (
 constexpr int kMaxQueries = 16;
 constexpr int kRowsMinGroup = 4;      // one query token: rows mode from this group size on (bf16)
 constexpr int kVectorMaxGroup = 8;    // vector path: query heads one workgroup holds
+constexpr int kWaveHeadsMinTiles = 32; // wave heads: tiles per wave, at least, on a full device
 
 // Everything the split kernel needs, by value.
 struct SplitArgs {
@@ -54,6 +56,10 @@ struct SplitArgs {
   int32_t num_queries;         // query tokens per sequence (rows mode; 1 otherwise)
   int32_t head_chunks;         // workgroups per (sequence, KV head, split): 1, or 2 when the
                                // vector path serves a group above kVectorMaxGroup heads
+  int32_t wave_heads;          // 1: a workgroup serves kWaves KV heads of one split, one per
+                               // wave, each wave streaming every tile of the split (h_kv is a
+                               // multiple of kWaves, head_chunks == 1); 0: one KV head, the
+                               // waves sharing its tiles
   float* logits;               // nullptr, or [B * h_q, logits_ld]: base-2 scores of every visited
                                // position (one query token per sequence only)
   int64_t logits_ld;           // multiple of kTile, >= max_ctx rounded up to kTile
@@ -126,6 +132,7 @@ struct Plan {
   int32_t num_queries;  // query tokens per sequence (>= 1)
   int32_t row_blocks;   // rows mode: blocks of 16 query rows per (sequence, KV head)
   int32_t head_chunks;  // vector path: the group's query heads served by this many workgroups
+  int32_t wave_heads;   // 1: each wave of a split workgroup serves its own KV head (SplitArgs)
   int64_t grid_split;
   int64_t grid_merge;
   uint64_t workspace_bytes;

@@ -212,7 +212,7 @@ void split_kernel(const SplitArgs a) {
   constexpr int KC = D / 32;                  // MFMA k-chunks (32 bf16 each)
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int q4 = lane >> 4;
 
@@ -224,6 +224,14 @@ void split_kernel(const SplitArgs a) {
   // h_kv is a multiple of 8, XCD k would otherwise see only KV heads k, k+8, ..., and with a
   // head-major paged cache whose blocks a sequence holds in physical order each XCD would read
   // the same few 4 KiB slices of every block (measured on MI355X: 0.67 of peak instead of 0.79).
+  //
+  // A token-major cache ([.., position, KV head, d]) interleaves the KV heads' rows of every
+  // position. Workgroups that each stream one KV head then read 1 / h_kv of every position's
+  // row, and as they drift apart over a split the rows of a position are fetched at scattered
+  // times (measured on MI355X, loads only: 0.79-0.84 of peak against 0.86 head-major). With
+  // wave_heads a workgroup serves kWaves KV heads of one split instead, wave w taking KV head
+  // kvh0 + w and every tile of the split, so the rows of each position are read together
+  // (0.87 in the same measurement); each wave's state is then a split state of its own.
   const int S = a.num_splits;
   const int units = int(gridDim.x) / S;
   const int split = blockIdx.x / units;
@@ -233,8 +241,12 @@ void split_kernel(const SplitArgs a) {
   const int hcn = a.head_chunks;
   const int hc = unit % hcn;
   const int unit_kv = unit / hcn;
-  const int b = unit_kv / a.h_kv;
-  const int kvh = (unit_kv - b * a.h_kv + split) % a.h_kv;
+  const bool wave_heads = a.wave_heads != 0;
+  const int hpu = wave_heads ? kWaves : 1;      // KV heads per workgroup
+  const int units_b = a.h_kv / hpu;             // workgroups per (sequence, split)
+  const int b = unit_kv / units_b;
+  const int kvh0 = ((unit_kv - b * units_b + split) % units_b) * hpu;
+  const int kvh = kvh0 + (wave_heads ? wave : 0);  // this wave's KV head
   const int h0 = hc * G;
   const int g = hcn > 1 ? min(G, a.group - h0) : a.group;  // query heads this workgroup serves
   const bool paged = PAGED == 2 ? (a.block_table != nullptr) : (PAGED == 1);
@@ -257,29 +269,35 @@ void split_kernel(const SplitArgs a) {
   const int ntiles = n_first + max((ctx + kTile - 1) / kTile - win_tile0, 0);
   const int t_begin = split * a.split_tiles;
   const int rows = nq * g;  // query rows of this (sequence, KV head): token-major, then head
-  // Global row of query row rho: token rho / g of sequence b, head kvh * g + rho % g.
-  auto out_row = [&](int rho) __attribute__((always_inline)) {
+  // Global row of query row rho of KV head kv: token rho / g of sequence b, head kv * g + rho % g.
+  auto out_row_of = [&](int kv, int rho) __attribute__((always_inline)) {
     if constexpr (ROWS)
-      return (int64_t(b) * nq + rho / g) * a.h_q + int64_t(kvh) * g + rho % g;
+      return (int64_t(b) * nq + rho / g) * a.h_q + int64_t(kv) * g + rho % g;
     else
-      return int64_t(b) * a.h_q + int64_t(kvh) * a.group + h0 + rho;
+      return int64_t(b) * a.h_q + int64_t(kv) * a.group + h0 + rho;
   };
+  auto out_row = [&](int rho) __attribute__((always_inline)) { return out_row_of(kvh, rho); };
   if (t_begin >= ntiles) {
     // Only an empty sequence reaches here with one split: its rows are defined as zeros.
     if (S == 1) {
-      for (int idx = threadIdx.x; idx < rows * D; idx += kSplitThreads)
-        a.out[out_row(idx / D) * D + idx % D] = 0.f;
-      if (SCORES && a.row_stats != nullptr && threadIdx.x < rows) {
-        a.row_stats[out_row(threadIdx.x) * 2 + 0] = neg_inf();
-        a.row_stats[out_row(threadIdx.x) * 2 + 1] = 0.f;
+      for (int idx = threadIdx.x; idx < hpu * rows * D; idx += kSplitThreads) {
+        const int r = idx / D;
+        a.out[out_row_of(kvh0 + r / rows, r % rows) * D + idx % D] = 0.f;
+      }
+      if (SCORES && a.row_stats != nullptr && threadIdx.x < hpu * rows) {
+        const int64_t row = out_row_of(kvh0 + threadIdx.x / rows, threadIdx.x % rows);
+        a.row_stats[row * 2 + 0] = neg_inf();
+        a.row_stats[row * 2 + 1] = 0.f;
       }
     }
     return;
   }
   const int t_end = min(t_begin + a.split_tiles, ntiles);
-  const int first = t_begin + wave;                                   // this wave's first tile
-  const int n_w = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
-  // Tile k of this wave is tile (wave + kWaves*k + rot) mod span of the split. The splits of a
+  const int wstride = wave_heads ? 1 : kWaves;  // tiles between this wave's consecutive tiles
+  const int woff = wave_heads ? 0 : wave;
+  const int first = t_begin + woff;                                   // this wave's first tile
+  const int n_w = first < t_end ? (t_end - first + wstride - 1) / wstride : 0;
+  // Tile k of this wave is tile (woff + wstride*k + rot) mod span of the split. The splits of a
   // sequence all start at once; in a paged cache whose blocks a sequence holds in physical order
   // they would then read addresses a fixed power-of-two stride apart at every step and crowd the
   // same memory channels. A split-dependent start (an odd multiple of the split index) breaks
@@ -289,7 +307,7 @@ void split_kernel(const SplitArgs a) {
   const int span = t_end - t_begin;
   const int rot = span > 0 ? int((int64_t(split) * 61) % span) : 0;
   auto visit = [&](int k) __attribute__((always_inline)) {
-    int j = wave + kWaves * k + rot;
+    int j = woff + wstride * k + rot;
     if (j >= span) j -= span;
     return t_begin + j;
   };
@@ -740,6 +758,35 @@ void split_kernel(const SplitArgs a) {
     }
   }
   __syncthreads();
+  if (wave_heads) {
+    // Every wave's state is a split state of its own KV head, kvh0 + w.
+    for (int idx = threadIdx.x; idx < kWaves * rows * D; idx += kSplitThreads) {
+      const int r = idx / D;
+      const int e = idx % D;
+      const int w = r / rows;
+      const int j = r - w * rows;
+      const float M = sm_m[w][j];
+      const bool seen = M != neg_inf();  // a row that saw no position: L = 0, output 0
+      const float L = seen ? sm_l[w][j] : 0.f;
+      const float acc = seen ? sm_o[w][j][e] : 0.f;
+      const int64_t row = out_row_of(kvh0 + w, j);
+      if (S == 1) {
+        a.out[row * D + e] = L > 0.f ? acc / L : 0.f;
+        if (SCORES && a.row_stats != nullptr && e == 0) {
+          a.row_stats[row * 2 + 0] = M;
+          a.row_stats[row * 2 + 1] = L;
+        }
+      } else {
+        const int64_t slot = row * S + split;
+        a.o_part[slot * D + e] = acc;
+        if (e == 0) {
+          a.ml_part[slot * 2 + 0] = M;
+          a.ml_part[slot * 2 + 1] = L;
+        }
+      }
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < rows * D; idx += kSplitThreads) {
     const int j = idx / D;
     const int e = idx % D;

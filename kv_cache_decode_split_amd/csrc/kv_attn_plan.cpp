@@ -133,23 +133,53 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   // registers; above kVectorMaxGroup heads that spilled hundreds of registers to scratch, so
   // two workgroups then serve the halves of the group (each reading the KV head once).
   if (plan->variant == 0 && g > kVectorMaxGroup) plan->head_chunks = 2;
-  const int64_t work_units = units * plan->head_chunks;
+  // Wave heads: a split workgroup serves kWaves KV heads, one per wave, each wave streaming a
+  // whole split, so that the rows of one position (token-major) or kWaves adjacent head slices of
+  // one block (head-major) are read together. MI355X, split kernel, fraction of peak:
+  //  * token-major: C5 0.72 -> 0.83, C2 0.74 -> 0.84, C3 0.82 -> 0.86, C3 with a 2048-position
+  //    window 0.73 -> 0.82, C5 with 4 tokens 0.70 -> 0.77; C4 (1024 units, ragged) drops from
+  //    0.80 to 0.68 at every split count tried, so kWaves * num_cus units or more keep one KV
+  //    head per workgroup;
+  //  * head-major, few units (long sequences split for parallelism): C5 0.824 -> 0.843, with
+  //    groups 1 and 4 0.83 -> 0.85, with blocks in physical order 0.81 -> 0.86; C3 (512 units)
+  //    unchanged, C2 (256 units, unsplit) 0.87 -> 0.84 and two-block rows mode (C5 with 4
+  //    tokens) 0.80 -> 0.77, so head-major takes it only with few units, one row block and at
+  //    least kWaves * kMaxSplitTiles tiles (16384 positions);
+  //  * both: when a device's worth of such workgroups leaves each wave only a few tiles the
+  //    step is latency-bound and the longer per-wave chains cost more than they gain (C5 with
+  //    a 4096-position window, ~9 tiles per wave: 16.3 -> 19.2 us token-major, 15.0 -> 19.1 us
+  //    head-major; C1 adds a merge pass), so each wave must get kWaveHeadsMinTiles tiles.
+  const bool token_major = p->k_stride_head < p->k_stride_token && p->v_stride_head < p->v_stride_token;
+  // KV_ATTN_WAVE_HEADS=0 / =1 overrides the choice (=1: whenever the shape allows it).
+  const char* wh_env = getenv("KV_ATTN_WAVE_HEADS");
+  const int wh_force = wh_env == nullptr ? -1 : strcmp(wh_env, "1") == 0 ? 1 : strcmp(wh_env, "0") == 0 ? 0 : -1;
+  const int64_t per_cu = plan->row_blocks == 2 ? 2 : 1;  // split workgroups per CU (see below)
+  const bool long_waves = tiles_max * (units / kWaves) >= int64_t(kWaveHeadsMinTiles) * num_cus * per_cu;
+  const bool wave_heads_fit = token_major
+      ? units < int64_t(kWaves) * num_cus
+      : units * 2 < num_cus && plan->row_blocks < 2 && tiles_max >= int64_t(kWaves) * kMaxSplitTiles;
+  const bool wave_heads_ok = p->num_kv_heads % kWaves == 0 && plan->head_chunks == 1;
+  plan->wave_heads = wave_heads_ok && (wh_force >= 0 ? wh_force == 1 : wave_heads_fit && long_waves) ? 1 : 0;
+  // Split workgroups per split.
+  const int64_t work_units = plan->wave_heads ? units / kWaves : units * plan->head_chunks;
 
   int64_t S;
   if (p->num_splits > 0) {
     S = p->num_splits;
   } else {
-    // About one split workgroup per CU; two for two-block rows mode, which keeps one tile in
-    // flight per wave and needs two waves per SIMD to keep enough loads outstanding.
-    const int64_t per_cu = plan->row_blocks == 2 ? 2 : 1;
+    // About one split workgroup per CU (per_cu); two for two-block rows mode, which keeps one
+    // tile in flight per wave and needs two waves per SIMD to keep enough loads outstanding.
     S = ceil_div(int64_t(num_cus) * per_cu, work_units);
     // Split length cap: 256 tiles keep a batch of many (sequence, KV head) units balanced when
     // its lengths are ragged; with few units (long sequences split for parallelism) or several
     // query tokens (heavier per-split epilogue and merge rows) 512 tiles stream faster. MI355X
     // sweeps: C4 (1024 units, ragged) best at 256; C5 (32 units) 0.825 at 512 against 0.815;
     // C3 with 8 tokens 0.828 against 0.776, C5 with 4 tokens 0.807 against 0.755.
-    const int64_t cap = (nq > 1 || work_units * 2 < num_cus) ? kMaxSplitTilesLong : kMaxSplitTiles;
-    const int64_t most = ceil_div(tiles_max, kMinSplitTiles);  // splits of >= 16 tiles
+    const int64_t cap = (plan->wave_heads || nq > 1 || work_units * 2 < num_cus) ? kMaxSplitTilesLong
+                                                                                 : kMaxSplitTiles;
+    // Splits of >= 16 tiles (>= 4 per wave); with wave heads every wave streams the whole
+    // split, so >= 4 tiles.
+    const int64_t most = ceil_div(tiles_max, plan->wave_heads ? kMinSplitTiles / kWaves : kMinSplitTiles);
     const int64_t least = ceil_div(tiles_max, cap);
     if (S > most) S = most;
     if (S < least) S = least;

@@ -115,7 +115,7 @@ class kv_attn_plan(ctypes.Structure):
         ("kernel_variant", ctypes.c_int32),
         ("group_padded", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("wave_heads", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
         ("ml_offset", ctypes.c_uint64),
     ]
@@ -210,7 +210,7 @@ def kv_attn_get_plan(params: kv_attn_params, num_cus: int = 0) -> dict:
     st = _lib.kv_attn_get_plan(ctypes.byref(params), int(num_cus), ctypes.byref(plan))
     if st != KV_ATTN_OK:
         raise KvAttnError(st, "kv_attn_get_plan")
-    return {name: getattr(plan, name) for name, _ in kv_attn_plan._fields_ if name != "reserved"}
+    return {name: getattr(plan, name) for name, _ in kv_attn_plan._fields_}
 
 
 def kv_attn_workspace_size(params: kv_attn_params) -> int:

@@ -138,7 +138,10 @@ def test_plan_with_several_query_tokens(nq, hq, hkv):
     assert L <= 8192 and one["split_len"] <= 8192   # splits of at most 512 tiles
     # two row blocks keep one tile in flight per wave: about two workgroups per CU
     per_cu = 2 if nq * (hq // hkv) > 16 else 1
-    assert plan["grid_split"] == B * hkv * S >= per_cu * 256
+    # one row block, few units and >= 1024 tiles: each wave streams a split of its own KV head
+    wh = per_cu == 1 and T // 16 >= 1024
+    assert plan["wave_heads"] == int(wh)
+    assert plan["grid_split"] == B * hkv * S // (4 if wh else 1) >= per_cu * 256
     if S > 1:
         assert plan["grid_merge"] == B * nq * hq
         assert plan["workspace_bytes"] >= B * nq * hq * S * (128 + 2) * 4
@@ -178,11 +181,16 @@ def test_plan_covers_every_tile_and_respects_bounds():
             plan = K.kv_attn_get_plan(p, cus)
             tiles = (T + 15) // 16
             S, L = plan["num_splits"], plan["split_len"]
+            # head-major: each wave its own KV head with few units and >= 1024 tiles
+            wh = (hkv % 4 == 0 and B * hkv * 2 < cus and tiles >= 1024
+                  and tiles * (B * hkv // 4) >= 32 * cus)
+            assert plan["wave_heads"] == int(wh), (B, hkv, T, cus)
             assert L % 16 == 0 and S >= 1
             assert S * L >= T and (S - 1) * L < T          # every position in exactly one split
-            assert plan["grid_split"] == B * hkv * S
+            assert plan["grid_split"] == B * hkv * S // (4 if wh else 1)
             if S > 1:
-                assert L // 16 >= min(16, tiles)             # splits of >= 16 tiles when possible
+                # splits of >= 16 tiles when possible (>= 4 per wave either way)
+                assert L // 16 >= min(4 if wh else 16, tiles)
                 assert plan["workspace_bytes"] >= B * hkv * 2 * S * (128 + 2) * 4
                 assert plan["grid_merge"] == B * hkv * 2
             else:
@@ -220,12 +228,16 @@ def test_random_plans_cover_the_visited_tiles_within_the_bounds():
         assert L % 16 == 0 and 1 <= S <= 4096, label
         assert S * (L // 16) >= bound and (S - 1) * (L // 16) < bound, label
         assert L // 16 <= 512 or S == 4096, label
+        wh = (hkv % 4 == 0 and B * hkv * 2 < cus and nq * g <= 16 and bound >= 1024
+              and bound * (B * hkv // 4) >= 32 * cus)
+        assert plan["wave_heads"] == int(wh), label
         if S > 1:
-            assert S <= -(-bound // 16), label   # at most one split per 16 visited tiles
+            # at most one split per 16 visited tiles (per 4 when every wave streams a split)
+            assert S <= -(-bound // (4 if wh else 16)), label
             rows = B * nq * hkv * g
             assert plan["grid_merge"] == rows
             assert plan["workspace_bytes"] >= rows * S * (128 + 2) * 4, label
-        assert plan["grid_split"] == B * hkv * S, label
+        assert plan["grid_split"] == B * hkv * S // (4 if wh else 1), label
 
 
 def test_plan_for_the_five_workloads():
@@ -235,7 +247,7 @@ def test_plan_for_the_five_workloads():
         (8, 32, 32, 4096): (1, 4096),
         (64, 32, 8, 8192): (2, 4096),
         (128, 32, 8, 32768): (8, 4096),
-        (4, 64, 8, 131072): (16, 8192),    # few units: splits of up to 512 tiles
+        (4, 64, 8, 131072): (32, 4096),    # few units: each wave streams a split of its own KV head
     }
     for (B, hq, hkv, T), (S, L) in want.items():
         p = _params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
@@ -244,6 +256,84 @@ def test_plan_for_the_five_workloads():
         assert (plan["num_splits"], plan["split_len"]) == (S, L)
         # groups of 4 or more run P.V on the matrix cores too (rows mode)
         assert plan["kernel_variant"] == (2 if hq // hkv >= 4 else 1)
+
+
+def _token_major(hkv, d=128, bs=16):
+    return dict(k_strides=(bs * hkv * d, hkv * d, d), v_strides=(bs * hkv * d, hkv * d, d))
+
+
+def test_token_major_plan_gives_each_wave_its_own_kv_head():
+    """Token-major caches with h_kv a multiple of 4 and fewer than 4 units per CU: four KV heads
+    per split workgroup, one per wave, each wave streaming a whole split."""
+    p = _params(batch=4, num_q_heads=64, num_kv_heads=8, max_ctx_len=131072,
+                max_blocks_per_seq=8192, num_blocks=10**6, **_token_major(8))
+    plan = K.kv_attn_get_plan(p, 256)
+    assert plan["wave_heads"] == 1
+    assert (plan["num_splits"], plan["split_len"]) == (32, 4096)   # 8 workgroups per split
+    assert plan["grid_split"] == 4 * 2 * 32 and plan["grid_merge"] == 4 * 64
+    for (B, hq, hkv, T), S in {(8, 32, 32, 4096): 4, (64, 32, 8, 8192): 2}.items():
+        p = _params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
+                    max_blocks_per_seq=T // 16, num_blocks=10**6, **_token_major(hkv))
+        plan = K.kv_attn_get_plan(p, 256)
+        assert plan["wave_heads"] == 1 and plan["num_splits"] == S, (B, hkv)
+    # 4 * num_cus units or more (C4's 1024) keep one KV head per workgroup
+    p = _params(batch=128, num_q_heads=32, num_kv_heads=8, max_ctx_len=32768,
+                max_blocks_per_seq=2048, num_blocks=10**6, **_token_major(8))
+    assert K.kv_attn_get_plan(p, 256)["wave_heads"] == 0
+    assert K.kv_attn_get_plan(p, 257)["wave_heads"] == 1
+    # head-major: only with few units, one row block and >= 1024 tiles
+    hm = dict(batch=4, num_q_heads=64, num_kv_heads=8, max_ctx_len=131072,
+              max_blocks_per_seq=8192, num_blocks=10**6)
+    assert K.kv_attn_get_plan(_params(**hm), 256)["wave_heads"] == 1
+    two_blocks = K.kv_attn_get_plan(_params(**hm, num_queries=4), 256)
+    assert two_blocks["wave_heads"] == 0 and two_blocks["num_splits"] == 16
+    assert K.kv_attn_get_plan(_params(**dict(hm, max_ctx_len=16368)), 256)["wave_heads"] == 0
+    assert K.kv_attn_get_plan(_params(**dict(hm, max_ctx_len=16369)), 256)["wave_heads"] == 1
+    assert K.kv_attn_get_plan(_params(**hm, window=4096, num_sinks=4), 256)["wave_heads"] == 0
+    # too little work per wave on a full device (a 4096-position window, 256 positions)
+    assert K.kv_attn_get_plan(_params(**hm, window=4096, num_sinks=4, **_token_major(8)),
+                              256)["wave_heads"] == 0
+    assert K.kv_attn_get_plan(_params(batch=1, num_q_heads=8, num_kv_heads=8, max_ctx_len=256,
+                                      max_blocks_per_seq=16, **_token_major(8)), 256)["wave_heads"] == 0
+    many = dict(batch=8, num_q_heads=32, num_kv_heads=32, max_ctx_len=4096, max_blocks_per_seq=256)
+    assert K.kv_attn_get_plan(_params(**many), 256)["wave_heads"] == 0
+    assert K.kv_attn_get_plan(_params(**many, **_token_major(32)), 256)["wave_heads"] == 1
+    # h_kv not a multiple of 4, or the vector path's halves: one KV head per workgroup
+    assert K.kv_attn_get_plan(_params(num_q_heads=4, num_kv_heads=2, **_token_major(2)), 256)["wave_heads"] == 0
+    p = _params(num_q_heads=8 * 16, q_dtype=K.KV_ATTN_F32, **_token_major(8))
+    assert K.kv_attn_get_plan(p, 256)["wave_heads"] == 0
+    # a caller-given split count is kept
+    p = _params(num_splits=3, max_ctx_len=20000, max_blocks_per_seq=1250, num_blocks=10**6,
+                **_token_major(8))
+    plan = K.kv_attn_get_plan(p, 256)
+    assert plan["wave_heads"] == 1 and plan["num_splits"] == 3 and plan["grid_split"] == 4 * 2 * 3
+
+
+def test_random_token_major_plans_cover_the_tiles():
+    rnd = np.random.default_rng(23)
+    for _ in range(300):
+        B = int(rnd.integers(1, 200))
+        hkv = int(rnd.choice([4, 8, 12, 32]))
+        g = int(rnd.choice([1, 2, 4, 8]))
+        T = int(rnd.choice([1, 15, 17, 300, 4096, 32768, 131072, 1 << 20]))
+        W = int(rnd.choice([0, 0, 64, 4096]))
+        cus = int(rnd.choice([1, 64, 256, 304]))
+        p = _params(batch=B, num_q_heads=hkv * g, num_kv_heads=hkv, max_ctx_len=T,
+                    max_blocks_per_seq=(T + 15) // 16, num_blocks=10**7, window=W or None,
+                    num_sinks=4, **_token_major(hkv))
+        plan = K.kv_attn_get_plan(p, cus)
+        all_tiles = (T + 15) // 16
+        bound = all_tiles if W == 0 else min(all_tiles, 1 + (W + 15) // 16 + 1)
+        S, L = plan["num_splits"], plan["split_len"]
+        label = (B, hkv, g, T, W, cus, S, L)
+        wh = B * hkv < 4 * cus and bound * (B * hkv // 4) >= 32 * cus
+        assert plan["wave_heads"] == int(wh), label
+        assert L % 16 == 0 and 1 <= S <= 4096, label
+        assert S * (L // 16) >= bound and (S - 1) * (L // 16) < bound, label
+        assert L // 16 <= 512 or S == 4096, label
+        assert plan["grid_split"] == (B * (hkv // 4) if wh else B * hkv) * S, label
+        if S > 1:
+            assert plan["workspace_bytes"] >= B * hkv * g * S * (128 + 2) * 4, label
 
 
 def test_explicit_split_count_and_variant_selection():

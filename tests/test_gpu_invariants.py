@@ -54,7 +54,8 @@ def test_single_position_is_bit_exact(name, num_splits):
 
 
 def _contiguous_copy(w):
-    """The same logical cache as ``w`` (paged) laid out contiguously, head-major."""
+    """The same logical cache as ``w`` (paged) laid out contiguously, in the same layout (so
+    that the plan maps the work the same way)."""
     spec = w.spec
     B, hkv, d = spec.batch, spec.num_kv_heads, spec.head_dim
     T = w.max_ctx_len
@@ -71,7 +72,9 @@ def _contiguous_copy(w):
         slot = (t % bs).cuda()
         ks[b, :, :n] = kv[blk, slot].permute(1, 0, 2)
         vs[b, :, :n] = vv[blk, slot].permute(1, 0, 2)
-    c = W.Workload(spec=W.preset(spec.name, paged=False, layout="head_major"), q=w.q, k_cache=ks,
+    if spec.layout == "token_major":
+        ks, vs = ks.permute(0, 2, 1, 3).contiguous(), vs.permute(0, 2, 1, 3).contiguous()
+    c = W.Workload(spec=W.preset(spec.name, paged=False, layout=spec.layout), q=w.q, k_cache=ks,
                    v_cache=vs, block_table=None, ctx_lens=w.ctx_lens, block_size=T, num_blocks=B)
     return c
 
@@ -89,14 +92,22 @@ def test_paged_equals_contiguous_bitwise(layout, num_splits):
     assert torch.equal(a, b)
 
 
-def test_head_major_equals_token_major_bitwise():
-    require_gpu()
-    hm = W.make_workload(W.preset("C5", batch=2, ctx=(2000, 1777), layout="head_major"), device="cuda")
+@pytest.mark.parametrize("wave_heads", [False, True])
+def test_head_major_equals_token_major_bitwise(monkeypatch, wave_heads):
+    """With the same mapping (one KV head per workgroup, or one per wave for both layouts) the
+    layout changes addresses only."""
+    K = require_gpu()
+    monkeypatch.setenv("KV_ATTN_WAVE_HEADS", "1" if wave_heads else "0")
+    ctx = (2000, 1777)
+    hm = W.make_workload(W.preset("C5", batch=2, ctx=ctx, layout="head_major"), device="cuda")
     tm_k = hm.k_cache.permute(0, 2, 1, 3).contiguous()  # [N, bs, hkv, d]
     tm_v = hm.v_cache.permute(0, 2, 1, 3).contiguous()
-    tm = W.Workload(spec=W.preset("C5", batch=2, ctx=(2000, 1777), layout="token_major"), q=hm.q,
+    tm = W.Workload(spec=W.preset("C5", batch=2, ctx=ctx, layout="token_major"), q=hm.q,
                     k_cache=tm_k, v_cache=tm_v, block_table=hm.block_table, ctx_lens=hm.ctx_lens,
                     block_size=hm.block_size, num_blocks=hm.num_blocks)
+    out = torch.empty(hm.q.shape, dtype=torch.float32, device="cuda")
+    plans = [K.decode_call_for(x, out).plan() for x in (hm, tm)]
+    assert plans[0] == plans[1] and plans[0]["wave_heads"] == int(wave_heads)
     assert torch.equal(run(hm), run(tm))
 
 

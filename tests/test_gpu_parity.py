@@ -40,6 +40,13 @@ SMALL = [
     ("C4", dict(batch=3, ctx=(900, 1, 450), num_q_heads=96, num_kv_heads=8, q_dtype="f32")),
     ("C4", dict(batch=6, ctx=("uniform", 1, 700), block_order="sequential", num_kv_heads=16,
                 num_q_heads=32)),
+    # token-major caches with h_kv a multiple of 4 (rows mode, MFMA scores with VALU P.V, the
+    # vector path, and a contiguous cache)
+    ("C5", dict(batch=2, ctx=(3000, 2999), layout="token_major")),
+    ("C2", dict(batch=2, ctx=(1500, 33), num_q_heads=8, num_kv_heads=8, layout="token_major")),
+    ("C1", dict(batch=3, ctx=(700, 1, 333), head_dim=128, num_q_heads=32, num_kv_heads=4,
+                q_dtype="f32", layout="token_major")),
+    ("C3", dict(batch=3, ctx=(1000, 17, 999), capacity=1000, layout="token_major")),
 ]
 
 
@@ -85,6 +92,45 @@ def _random_specs(n, seed=7):
 RANDOM = _random_specs(40)
 
 
+def _random_wave_head_specs(n, seed=8):
+    """Token-major caches with h_kv in {4, 8, 12}, each wave of a split workgroup serving its own
+    KV head (forced: the planner picks that for long sequences only)."""
+    rnd = random.Random(seed)
+    specs = []
+    for i in range(n):
+        hkv = rnd.choice([4, 8, 12])
+        g = rnd.choice([1, 2, 4, 8])
+        B = rnd.randint(1, 3)
+        paged = rnd.random() < 0.7
+        lens = tuple(rnd.randint(1, 3000) for _ in range(B))
+        qd, kd = rnd.choice([("bf16", "bf16"), ("bf16", "bf16"), ("f32", "f32"), ("f32", "bf16")])
+        specs.append(dict(
+            spec=W.WorkloadSpec(
+                name=f"wh{i}", batch=B, num_q_heads=g * hkv, num_kv_heads=hkv,
+                head_dim=rnd.choice([64, 128]), ctx=lens, paged=paged,
+                block_size=rnd.choice([16, 32]) if paged else 16, kv_dtype=kd, q_dtype=qd,
+                num_sinks=rnd.choice([0, 4]), layout="token_major", seed=5600 + i,
+                extra_blocks=rnd.randint(1, 4), capacity=None if paged else max(lens)),
+            num_splits=rnd.choice([0, 0, 1, 3])))
+    return specs
+
+
+RANDOM_WAVE_HEADS = _random_wave_head_specs(12)
+
+
+@pytest.mark.parametrize("case", RANDOM_WAVE_HEADS, ids=[c["spec"].name for c in RANDOM_WAVE_HEADS])
+def test_token_major_wave_heads_match_oracle(case, monkeypatch):
+    K = require_gpu()
+    monkeypatch.setenv("KV_ATTN_WAVE_HEADS", "1")
+    spec = case["spec"]
+    announce(f"wave heads {spec}")
+    w = W.make_workload(spec, device="cuda")
+    out = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+    assert K.decode_call_for(w, out, num_splits=case["num_splits"]).plan()["wave_heads"] == 1
+    got = run(w, num_splits=case["num_splits"])
+    check_close(got.cpu().numpy(), oracle_full(w), spec.name)
+
+
 @pytest.mark.parametrize("case", RANDOM, ids=[c["spec"].name for c in RANDOM])
 def test_random_shapes_match_oracle(case):
     require_gpu()
@@ -109,6 +155,7 @@ FULL = [
     ("C4", "extremes", [0, 7]),
     ("C5", [0, 3], [0, 5]),
     ("C5-sequential", [1, 2], [3, 7]),
+    ("C5-token_major", [0, 2], [2, 7]),
 ]
 
 
@@ -117,12 +164,16 @@ def test_full_size_workloads_on_sampled_rows(name, seqs, heads):
     """The bench's launch configuration (auto split plan) at full size; sampled rows checked.
 
     C4 samples its shortest, longest and a middle sequence. C2 is one of its 32 layers.
-    C5-sequential deals the blocks to the sequences in physical order.
+    C5-sequential deals the blocks to the sequences in physical order; C5-token_major stores
+    the cache token-major (each wave of a workgroup then serves its own KV head).
     """
     require_gpu()
     announce(f"full {name}")
-    base, _, order = name.partition("-")
-    spec = W.preset(base, block_order=order) if order else W.PRESETS[base]
+    base, _, variant = name.partition("-")
+    if variant == "token_major":
+        spec = W.preset(base, layout="token_major")
+    else:
+        spec = W.preset(base, block_order=variant) if variant else W.PRESETS[base]
     w = W.make_workload(spec, device="cuda")
     try:
         out = run(w)
