@@ -136,7 +136,7 @@ typedef struct kv_attn_plan {
   int32_t kernel_variant;   /* 0: fp32 vector path, 1: bf16 matrix-core (MFMA) scores,
                                2: bf16 MFMA scores and P.V ("rows mode": num_queries > 1, or
                                one token with a group of 4 or more query heads per KV head;
-                               kv_attn_decode_scores runs variant 1 in its place) */
+                               kv_attn_decode_scores runs the same variant) */
   int32_t group_padded;     /* compiled group width (power of two >= g; 8 for the halves above) */
   int32_t num_cus;          /* compute units the plan was made for */
   int32_t wave_heads;       /* 1: each split workgroup serves 4 KV heads, one per wave, every

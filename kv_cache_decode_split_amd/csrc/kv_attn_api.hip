@@ -187,14 +187,10 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
   ScoreLayout sl = {};
   if (scores) {
     if (plan.num_queries > 1) return KV_ATTN_ERR_UNSUPPORTED;  // one query token per sequence
-    // Score export is compiled into the one-token matrix-core kernel (variant 1), which every
-    // bf16 group up to 16 also runs correctly; the split count is the same for both variants.
-    if (plan.variant == 2) {
-      plan.variant = 1;
-      plan.row_blocks = 0;
-    }
-    // Score export is compiled for bf16 q and KV (matrix cores) and for fp32 q and KV.
-    const bool bf16_pair = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 && plan.variant == 1;
+    // Score export is compiled for bf16 q and KV (matrix cores: the one-token kernel, or rows
+    // mode with one block, which one token always fits) and for fp32 q and KV.
+    const bool bf16_pair = p->q_dtype == KV_ATTN_BF16 && p->kv_dtype == KV_ATTN_BF16 &&
+                           (plan.variant == 1 || (plan.variant == 2 && plan.row_blocks == 1));
     const bool f32_pair = p->q_dtype == KV_ATTN_F32 && p->kv_dtype == KV_ATTN_F32;
     if (!bf16_pair && !f32_pair) return KV_ATTN_ERR_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(token_scores) & 3u) != 0) return KV_ATTN_ERR_UNSUPPORTED;

@@ -202,7 +202,7 @@ void split_kernel(const SplitArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(!MFMA || (Q_BF16 && KV_BF16), "matrix-core scores need bf16 q and KV");
   static_assert(R == 0 || MFMA, "rows mode runs on the matrix cores");
-  static_assert(!(SCORES && R > 0), "score export takes one query token per sequence");
+  static_assert(!(SCORES && R > 1), "score export takes one query token per sequence");
   constexpr bool ROWS = R > 0;
   constexpr int NR = ROWS ? 16 * R : G;       // query rows held per (sequence, KV head)
   constexpr int EPL = D / 16;                 // elements per lane of a 16-lane row
@@ -633,6 +633,9 @@ void split_kernel(const SplitArgs a) {
           sc[r] = valid ? acc[r] * a.scale_log2 : neg_inf();
         }
       }
+      // Score export (one token, one block: query row r16 is head r16): the same lane layout as
+      // the one-token kernel's scores, positions p0 + 4*q4 .. +3.
+      if constexpr (SCORES) store_scores(f32x4_t{sc[0], sc[1], sc[2], sc[3]}, p0 + 4 * q4, r16);
       float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mt = max_xor32(max_xor16(mt));
       const float m_new = fmaxf(m_r[cb], mt);
@@ -1043,9 +1046,15 @@ int launch_scores_variant(const SplitArgs& a, const Plan& plan, bool paged, bool
   return int(hipErrorInvalidValue);
 }
 
-// Rows mode (several query tokens per sequence): bf16 only, 1 or 2 blocks of 16 query rows.
+// Rows mode (several query tokens per sequence, or one token with a group of 4 or more): bf16
+// only, 1 or 2 blocks of 16 query rows; score export (one token) in one block.
 template <int D>
 int launch_rows(const SplitArgs& a, const Plan& plan, bool paged, hipStream_t s) {
+  if (a.logits != nullptr) {
+    if (plan.row_blocks != 1 || plan.num_queries != 1) return int(hipErrorInvalidValue);
+    return paged ? launch_one<D, 1, true, true, true, 1, 1, true>(a, plan.grid_split, s)
+                 : launch_one<D, 1, true, true, true, 0, 1, true>(a, plan.grid_split, s);
+  }
   switch (plan.row_blocks) {
     case 1: return paged ? launch_one<D, 1, true, true, true, 1, 1>(a, plan.grid_split, s)
                          : launch_one<D, 1, true, true, true, 0, 1>(a, plan.grid_split, s);

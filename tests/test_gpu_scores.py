@@ -30,14 +30,11 @@ def _oracle_scores(w, seqs=None, kv_heads=None):
 
 
 def _check_output(out, w, num_splits, label):
-    """The output of a score-export call: the plain decode's bits when that runs the same
-    one-token kernel, else within the parity tolerance of the oracle."""
-    K = require_gpu()
-    plain_call = K.decode_call_for(w, torch.empty_like(out), num_splits=num_splits)
-    if plain_call.plan()["kernel_variant"] != 2:
-        assert torch.equal(out, run(w, num_splits=num_splits)), "score export changed the output"
-    else:
-        check_close(out.cpu().numpy(), oracle_full(w), f"{label} output")
+    """The output of a score-export call: the plain decode's bits (score export runs the same
+    kernel variant and plan, with the score stores added), and within the parity tolerance of
+    the oracle."""
+    assert torch.equal(out, run(w, num_splits=num_splits)), "score export changed the output"
+    check_close(out.cpu().numpy(), oracle_full(w), f"{label} output")
 
 
 def _run_scores(w, accumulate=False, fill=float("nan"), **kwargs):
