@@ -49,6 +49,7 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (unique KV bytes/time) + decode-attn µs/step"
 HBM_PEAK_GBPS = 8000.0
+LLC_BYTES = 256 << 20  # MI355X last-level cache (MALL, "Infinity Cache")
 KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_decode_split_amd", "csrc", f)
                   for f in ("kv_attn_kernels.hip", "kv_attn_internal.h", "kv_attn_plan.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -84,6 +85,8 @@ def parse_args():
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip timing the library's read probe (the practical read ceiling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline time budget")
     ap.add_argument("--append", action="store_true",
                     help="each layer first appends the current token's K/V (kv_attn_append_decode)")
@@ -249,16 +252,39 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # An event at every step boundary: the first and last bracket the K steps (ms_per_step), the
+    # ones between give each step's duration for the spread.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         run_step()
-    e1.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_us = [1e3 * marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     print(f"[bench] pass A done: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # ---- cache state ------------------------------------------------------------------------------
+    # Steps run back to back, so a step whose inputs fit the 256 MB last-level cache (MALL) could
+    # find them there. When the bytes a step touches are under 4x that, the steps are timed once
+    # more one at a time, each after writing a 512 MiB scratch buffer (outside the timed region),
+    # so that they start cold.
+    touched = kv_bytes_step + sum(int(w.q.numel()) * w.q.element_size() * 2 for w in wls)
+    cold_us = None
+    if touched < 4 * LLC_BYTES:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_us = []
+        for _ in range(args.steps):
+            scratch.fill_(7)
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record()
+            run_step()
+            a1.record()
+            torch.cuda.synchronize()
+            cold_us.append(1e3 * a0.elapsed_time(a1))
+        del scratch
 
     # ---- pass B: the split kernel alone, launched back to back ------------------------------------
     # Two events bracket K rounds of split launches (each round: every layer's launch, repeated so
@@ -332,6 +358,29 @@ def main():
 
     finite = all(bool(torch.isfinite(o).all()) for o in outs)
 
+    # ---- practical read ceiling: the library's read probe on a 4 GiB buffer ------------------------
+    stream_ceiling = None
+    if not args.no_read_probe:
+        buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            K.kv_attn_read_probe(buf, sink)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        n_probe = 10
+        a.record()
+        for _ in range(n_probe):
+            K.kv_attn_read_probe(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        probe_us = 1e3 * a.elapsed_time(b) / n_probe
+        stream_ceiling = {"achieved": round(buf.numel() / (probe_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+                          "bytes_per_launch": buf.numel(), "avg_launch_us": round(probe_us, 2),
+                          "kernel": "kv_attn_read_probe (16-byte nontemporal loads, 1 MiB contiguous "
+                                    "per workgroup, no compute)"}
+        del buf, sink
+
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,8 +438,20 @@ def main():
             "avg_launch_us": round(split_us_avg, 2),
             "launches_timed": launches_timed,
             "timed_by": "host launches" if args.eager else "HIP graph replay",
+            "stream_ceiling": stream_ceiling,
+            "frac_of_stream_ceiling": (round(achieved / stream_ceiling["achieved"], 4)
+                                       if stream_ceiling else None),
         },
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "step_us_spread": _spread(step_us),
+        "cache": {
+            "bytes_touched_per_step": touched,
+            "state": ("streamed: a step touches more than 4x the 256 MB last-level cache; steps run "
+                      "back to back with no flush" if cold_us is None else
+                      "a step's bytes fit near the 256 MB last-level cache: ms_per_step is back to "
+                      "back (warm); cold_us_per_step times each step after writing 512 MiB"),
+            "cold_us_per_step": _spread(cold_us) if cold_us else None,
+        },
         "outputs_finite": finite,
         "cpu_baseline": cpu,
         "context": page_context(A, kv_bytes_step, ms_per_step),
@@ -406,6 +467,18 @@ def main():
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
     print(json.dumps(line), flush=True)
+
+
+def _spread(xs):
+    """p10 / median / p90 of per-step durations (µs)."""
+    ys = sorted(xs)
+
+    def q(f):
+        pos = f * (len(ys) - 1)
+        lo = int(pos)
+        hi = min(lo + 1, len(ys) - 1)
+        return round(ys[lo] + (ys[hi] - ys[lo]) * (pos - lo), 2)
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "n": len(ys)}
 
 
 def page_context(A, kv_bytes_step, ms_per_step):

@@ -324,6 +324,24 @@ kv_attn_status kv_attn_decode_scores(const void* q, const void* k_cache, const v
 kv_attn_status kv_attn_validate_host(const int32_t* block_table, const int32_t* ctx_lens,
                                      const kv_attn_params* p);
 
+/*
+ * Measurement aid, not part of attention: the practical read ceiling of the device. Streams
+ * `bytes` of device memory at `src` with the 16-byte nontemporal loads the split kernel uses for
+ * its KV tiles, in the most favourable order measured (each 256-thread workgroup reads one
+ * contiguous KV_ATTN_PROBE_CHUNK-byte range, four loads in flight per lane) and with no compute,
+ * enqueued on `stream`; timing a few launches with device events gives the rate a bare read
+ * stream reaches, against which the attention kernels' rates can be read as well as against the
+ * published peak.
+ * src   : device, 16-byte aligned, `bytes` readable (a positive multiple of 16; it is only read).
+ * sink  : device uint32 (one word); it may be overwritten with a meaningless value (the kernel
+ *         keeps its loads live with a store it practically never takes).
+ * Returns KV_ATTN_ERR_NULL for a NULL pointer, KV_ATTN_ERR_UNSUPPORTED for a misaligned `src`,
+ * a size that is 0 or not a multiple of 16, or more than 2^31 - 1 chunks, KV_ATTN_ERR_HIP if the
+ * launch fails.
+ */
+#define KV_ATTN_PROBE_CHUNK (1u << 20)
+kv_attn_status kv_attn_read_probe(const void* src, uint64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
-HIP_SOURCES = ["kv_attn_kernels.hip", "kv_attn_api.hip", "kv_evict.hip"]
+HIP_SOURCES = ["kv_attn_kernels.hip", "kv_attn_api.hip", "kv_evict.hip", "kv_probe.hip"]
 CXX_SOURCES = ["kv_attn_plan.cpp"]
 
 

@@ -38,6 +38,8 @@ __all__ = [
     "kv_attn_validate_host",
     "kv_attn_scores_workspace_size",
     "kv_attn_decode_scores",
+    "kv_attn_read_probe",
+    "KV_ATTN_PROBE_CHUNK",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -71,7 +73,10 @@ EXPORTED_SYMBOLS = (
     "kv_attn_validate_host",
     "kv_attn_scores_workspace_size",
     "kv_attn_decode_scores",
+    "kv_attn_read_probe",
 )
+
+KV_ATTN_PROBE_CHUNK = 1 << 20
 
 
 class KvAttnError(RuntimeError):
@@ -155,6 +160,8 @@ def _load():
     lib.kv_attn_decode_scores.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                           P(kv_attn_params), vp, ctypes.c_size_t, vp]
     lib.kv_attn_decode_scores.restype = ctypes.c_int
+    lib.kv_attn_read_probe.argtypes = [vp, ctypes.c_uint64, vp, vp]
+    lib.kv_attn_read_probe.restype = ctypes.c_int
     return lib
 
 
@@ -167,6 +174,19 @@ def kv_attn_abi_version() -> int:
 
 def kv_attn_status_string(status: int) -> str:
     return _lib.kv_attn_status_string(int(status)).decode()
+
+
+def kv_attn_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream every byte of ``src`` (a contiguous CUDA tensor) once with the read probe, on the
+    current stream; ``sink`` is a CUDA tensor with at least one 32-bit element."""
+    if not (src.is_cuda and sink.is_cuda and src.is_contiguous()):
+        raise ValueError("read probe: src and sink must be CUDA tensors, src contiguous")
+    if sink.numel() < 1 or sink.element_size() != 4:
+        raise ValueError("read probe: sink must hold a 32-bit word")
+    stream = torch.cuda.current_stream(src.device).cuda_stream
+    st = _lib.kv_attn_read_probe(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), stream)
+    if st != KV_ATTN_OK:
+        raise KvAttnError(st, "kv_attn_read_probe")
 
 
 def _dtype_code(dt: torch.dtype) -> int:

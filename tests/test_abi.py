@@ -438,3 +438,12 @@ def test_append_argument_errors_fail_before_any_hip_call():
                                      None) == K.KV_ATTN_ERR_NULL
     assert lib.kv_attn_append_decode(16, 8, 16, 16, 16, 16, 16, 16, ctypes.byref(p), None, 0,
                                      None) == K.KV_ATTN_ERR_UNSUPPORTED
+
+
+def test_read_probe_rejects_bad_arguments_before_any_hip_call():
+    lib = K._lib
+    assert lib.kv_attn_read_probe(None, 1 << 20, 16, None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_read_probe(16, 1 << 20, None, None) == K.KV_ATTN_ERR_NULL
+    assert lib.kv_attn_read_probe(16, 0, 16, None) == K.KV_ATTN_ERR_UNSUPPORTED
+    assert lib.kv_attn_read_probe(16, 1000, 16, None) == K.KV_ATTN_ERR_UNSUPPORTED   # not x16
+    assert lib.kv_attn_read_probe(8, 1 << 20, 16, None) == K.KV_ATTN_ERR_UNSUPPORTED  # misaligned
