@@ -628,7 +628,8 @@ def _blas_threads():
 def cpu_baseline(wls, spec, budget_s, elem, A):
     """The oracle, as it stands, on whole (layer, sequence, KV head) units of the workload, in
     order, until the time budget is spent (at least one unit). Host copies of each unit are made
-    outside the timed region. Returns the oracle's unique-KV GB/s."""
+    outside the timed region. Returns the oracle's unique-KV GB/s on the host's BLAS threads and,
+    for C1-C3, also on one thread (a third of the budget)."""
     from kv_cache_decode_split_amd import workloads as W
     from oracle import decode_attention, verify_attention
 
@@ -636,28 +637,38 @@ def cpu_baseline(wls, spec, budget_s, elem, A):
     units = [(l, b, h) for l in range(len(wls)) for b in range(spec.batch)
              for h in range(spec.num_kv_heads)]
     lens = [w.ctx_lens.cpu().tolist() for w in wls]
-    done_bytes, spent, n = 0, 0.0, 0
-    for l, b, h in units:
-        v = W.oracle_sample(wls[l], [b], [h])
-        t0 = time.perf_counter()
-        fn = decode_attention if gamma == 1 else verify_attention
-        fn(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
-           block_size=v["block_size"] if v["block_table"] is not None else None,
-           window=spec.window, num_sinks=spec.num_sinks)
-        spent += time.perf_counter() - t0
-        done_bytes += 2 * A.attended_length(lens[l][b], spec.window, spec.num_sinks,
-                                            gamma) * spec.head_dim * elem
-        n += 1
-        if spent >= budget_s:
-            break
-    return {
-        "value": round(done_bytes / spent / 1e9, 4),
-        "unit": "GB/s",
-        "cores": _blas_threads(),
-        "kind": "oracle",
-        "sample": f"{n} of {len(units)} (layer, sequence, KV head) units of {spec.name}, in order "
-                  f"({done_bytes} unique KV bytes, {spent:.1f} s of oracle time)",
-    }
+
+    def run(budget):
+        done_bytes, spent, n = 0, 0.0, 0
+        for l, b, h in units:
+            v = W.oracle_sample(wls[l], [b], [h])
+            t0 = time.perf_counter()
+            fn = decode_attention if gamma == 1 else verify_attention
+            fn(v["q"], v["k_cache"], v["v_cache"], v["ctx_lens"], v["block_table"],
+               block_size=v["block_size"] if v["block_table"] is not None else None,
+               window=spec.window, num_sinks=spec.num_sinks)
+            spent += time.perf_counter() - t0
+            done_bytes += 2 * A.attended_length(lens[l][b], spec.window, spec.num_sinks,
+                                                gamma) * spec.head_dim * elem
+            n += 1
+            if spent >= budget:
+                break
+        sample = (f"{n} of {len(units)} (layer, sequence, KV head) units of {spec.name}, in order "
+                  f"({done_bytes} unique KV bytes, {spent:.1f} s of oracle time)")
+        return round(done_bytes / spent / 1e9, 4), sample
+
+    value, sample = run(budget_s)
+    out = {"value": value, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle", "sample": sample}
+    if spec.name in ("C1", "C2", "C3"):
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:
+            threadpool_limits = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                v1, s1 = run(budget_s / 3)
+            out["single_thread"] = {"value": v1, "unit": "GB/s", "cores": 1, "sample": s1}
+    return out
 
 
 if __name__ == "__main__":
