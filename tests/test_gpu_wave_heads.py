@@ -109,3 +109,22 @@ def test_score_export_matches_oracle(name, over, num_splits):
     out, scores = _run_scores(w, num_splits=num_splits)
     check_close(scores.cpu().numpy(), _oracle_scores(w), f"scores {name} S={num_splits}")
     _check_output(out, w, num_splits, f"scores {name} S={num_splits}")
+
+
+@pytest.mark.parametrize("layout", ["head_major", "token_major"])
+def test_split_then_merge_equals_decode(layout):
+    K = require_gpu()
+    spec = W.preset("C5", batch=2, ctx=(5000, 3001), layout=layout)
+    w = W.make_workload(spec, device="cuda")
+    announce(f"wave heads split+merge vs decode {layout}")
+    a = torch.full(w.q.shape, float("nan"), device="cuda")
+    b = torch.full(w.q.shape, float("nan"), device="cuda")
+    call_a = K.decode_call_for(w, a, num_splits=4)
+    call_b = K.decode_call_for(w, b, num_splits=4)
+    assert call_a.plan()["wave_heads"] == 1 and call_a.plan()["num_splits"] == 4
+    call_a.decode()
+    call_b.split()
+    call_b.merge()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    check_close(a.cpu().numpy(), oracle_full(w), f"split+merge {layout}")
