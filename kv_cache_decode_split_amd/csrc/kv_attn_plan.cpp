@@ -173,7 +173,8 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
     // Split length cap: 256 tiles keep a batch of many (sequence, KV head) units balanced when
     // its lengths are ragged; with few units (long sequences split for parallelism) or several
     // query tokens (heavier per-split epilogue and merge rows) 512 tiles stream faster. MI355X
-    // sweeps: C4 (1024 units, ragged) best at 256; C5 (32 units) 0.825 at 512 against 0.815;
+    // sweeps: C4 (1024 units, ragged) best at 256; C5 (32 units, one KV head per workgroup)
+    // 0.825 at 512 against 0.815;
     // C3 with 8 tokens 0.828 against 0.776, C5 with 4 tokens 0.807 against 0.755.
     const int64_t cap = (plan->wave_heads || nq > 1 || work_units * 2 < num_cus) ? kMaxSplitTilesLong
                                                                                  : kMaxSplitTiles;
