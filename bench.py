@@ -124,7 +124,7 @@ def parse_args():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode-attention path has no multi-GPU component here).", file=sys.stderr)
         sys.exit(2)
 
