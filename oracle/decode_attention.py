@@ -16,7 +16,7 @@ Sources, by page title and section:
   - §4: under GQA several query heads share one KV head; the unique-KV traffic model assumes
     the shared KV is read once.
 
-Readings taken where the pages leave a point open (each is also listed in the design doc):
+Readings taken where the pages leave a point open:
 
 * GQA grouping: query head ``h`` reads KV head ``h // g`` with ``g = h_q // h_kv``.
 * ``d`` in 1/√d is the per-head dimension; a caller-given scale overrides it.

@@ -18,7 +18,7 @@ The page contrasts a naive selection (repeatedly scanning the table for the best
 with a single global sort; the oracle is the global sort: one library sort of the pool by that
 key, the first M − L·H entries kept.
 
-Readings taken where the page is silent (also listed in the design doc):
+Readings taken where the page is silent:
 
 * Scores are real numbers compared as values (so −0.0 and +0.0 tie and fall to the index
   tie-break); ±inf are allowed; NaN has no place in the order and is rejected.

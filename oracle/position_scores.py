@@ -8,7 +8,7 @@ a few "heavy hitter" tokens collect most of the attention mass), and the evictio
 one score per (layer, head, token). The weights themselves are the softmax of §19.4.1 / §19.6.2:
 P = softmax(scale · K q) over the attended positions.
 
-Readings taken where the page is silent (also listed in the design doc):
+Readings taken where the page is silent:
 
 * The unit that is kept or evicted is a KV head's entry, so the score of (sequence b, KV head
   kvh, position t) is the sum over the g query heads that share that KV head of the weight each

@@ -8,7 +8,7 @@ single forward pass (a γ×d-shaped product instead of γ sequential steps). The
 pass is what is computed here; the acceptance rule that follows it needs the models' output
 distributions and is not part of this path.
 
-Readings taken where the page is silent (also listed in the design doc):
+Readings taken where the page is silent:
 
 * The γ proposed tokens have been appended to the cache before the check, so ``ctx_lens[b]``
   (T) counts them: they are positions T−γ .. T−1, and query j (0-based) is the token at
