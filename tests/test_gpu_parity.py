@@ -156,6 +156,7 @@ FULL = [
     ("C5", [0, 3], [0, 5]),
     ("C5-sequential", [1, 2], [3, 7]),
     ("C5-token_major", [0, 2], [2, 7]),
+    ("C4-kv4", "extremes", [0, 3]),
 ]
 
 
@@ -165,13 +166,17 @@ def test_full_size_workloads_on_sampled_rows(name, seqs, heads):
 
     C4 samples its shortest, longest and a middle sequence. C2 is one of its 32 layers.
     C5-sequential deals the blocks to the sequences in physical order; C5-token_major stores
-    the cache token-major (each wave of a workgroup then serves its own KV head).
+    the cache token-major (each wave of a workgroup then serves its own KV head); C4-kv4 is C4's
+    ragged batch with 4 KV heads (group 4), whose split workgroups are dealt to the XCDs with
+    the per-split sequence shift.
     """
     require_gpu()
     announce(f"full {name}")
     base, _, variant = name.partition("-")
     if variant == "token_major":
         spec = W.preset(base, layout="token_major")
+    elif variant == "kv4":
+        spec = W.preset(base, num_q_heads=16, num_kv_heads=4)
     else:
         spec = W.preset(base, block_order=variant) if variant else W.PRESETS[base]
     w = W.make_workload(spec, device="cuda")
