@@ -27,10 +27,17 @@ with events, never time host submission):
   * with --gamma G (speculative-decoding verification) every sequence has G query tokens, the
     last G cached positions, each attending to its own prefix; bytes count the union of the
     positions they attend (each KV element once) and tokens_per_s counts B * G tokens;
+  * a workload whose bytes fit near the 256 MB last-level cache is also timed cold: each step,
+    and each split launch, alone after writing 512 MiB (``cache.cold_us_per_step`` and
+    ``roofline.cold``; ``roofline.cache`` then says that pass B ran warm);
   * cpu_baseline: the fp64 oracle (oracle/) timed on the host on a bounded sample of the same
     workload (whole (layer, sequence, KV head) units in order, about 15 s of CPU work).
 
-Prints one JSON line. Only one GPU is used; --gpus above 1 exits with a message.
+The plain default run (C2) also measures C3, C4 and C5 the same way, one after the other, and
+reports each in the line's ``configs`` object (its step time and rate, the split kernel's
+roofline fraction and counter traffic, and a CPU baseline of about 3 s); ``--also`` chooses
+other workloads or none. Prints one JSON line. Only one GPU is used; --gpus above 1 exits with
+a message.
 """
 
 from __future__ import annotations
@@ -51,7 +58,10 @@ METRIC = "achieved HBM GB/s (unique KV bytes/time) + decode-attn µs/step"
 HBM_PEAK_GBPS = 8000.0
 LLC_BYTES = 256 << 20  # MI355X last-level cache (MALL, "Infinity Cache")
 KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_decode_split_amd", "csrc", f)
-                  for f in ("kv_attn_kernels.hip", "kv_attn_internal.h", "kv_attn_plan.cpp")]
+                  for f in ("kv_attn_split.h", "kv_attn_split_mfma64.hip", "kv_attn_split_mfma128.hip",
+                            "kv_attn_split_vector64.hip", "kv_attn_split_vector128.hip",
+                            "kv_attn_split_rows.hip", "kv_attn_kernels.hip", "kv_attn_internal.h",
+                            "kv_attn_plan.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -83,6 +93,12 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None,
                     help="warm-up steps (default: enough for >= 0.25 s of GPU work, at least 5)")
     ap.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads measured after the main one and reported in "
+                         "the line's 'configs' object (default: C3,C4,C5 for the plain C2 run, "
+                         "none otherwise; '' for none)")
+    ap.add_argument("--also-cpu-seconds", type=float, default=3.0,
+                    help="CPU-baseline time budget of each --also workload")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true",
@@ -121,6 +137,9 @@ def parse_args():
     return ap.parse_args()
 
 
+VARIANT_FLAGS = ("window", "attn_sinks", "block_order", "layout", "scores", "append", "evict")
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -128,11 +147,8 @@ def main():
               "(the decode-attention path has no multi-GPU component here).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from kv_cache_decode_split_amd import accounting as A
-    from kv_cache_decode_split_amd import kv_attn as K
     from kv_cache_decode_split_amd import workloads as W
 
     if not torch.cuda.is_available():
@@ -142,15 +158,52 @@ def main():
     if args.evict is not None:
         bench_evict(args, W)
         return
-    spec = W.PRESETS[args.config]
-    tag = args.config
+    spec, tag = resolve_spec(args, args.config, W)
+    if args.scores and (args.append or args.gamma > 1):
+        print("bench.py: --scores takes one query token and no --append", file=sys.stderr)
+        sys.exit(2)
+    also = args.also
+    if also is None:  # the long-context workloads ride along with the plain headline run
+        plain = args.config == "C2" and args.gamma == 1 and args.num_splits == 0 and not any(
+            getattr(args, f) not in (None, False) for f in VARIANT_FLAGS)
+        also = "C3,C4,C5" if plain else ""
+    also = [c.strip() for c in also.split(",") if c.strip()]
+    for c in also:
+        if c not in W.PRESETS:
+            print(f"bench.py: --also names an unknown workload {c!r}", file=sys.stderr)
+            sys.exit(2)
+
+    line = measure_decode(args, spec, tag, cpu_budget=None if args.no_cpu_baseline else args.cpu_seconds,
+                          single_thread=True)
+    ceiling = None if args.no_read_probe else read_ceiling()
+    extras = {}
+    for c in also:
+        extra_spec, extra_tag = resolve_spec(args, c, W)
+        extras[c] = measure_decode(args, extra_spec, extra_tag,
+                                   cpu_budget=None if args.no_cpu_baseline else args.also_cpu_seconds,
+                                   single_thread=False)
+    for ln in [line, *extras.values()]:
+        roof = ln["roofline"]
+        roof["stream_ceiling"] = ceiling
+        roof["frac_of_stream_ceiling"] = (round(roof["achieved"] / ceiling["achieved"], 4)
+                                          if ceiling else None)
+    if extras:
+        line["configs"] = {c: config_summary(ln) for c, ln in extras.items()}
+    print(json.dumps(line), flush=True)
+
+
+def resolve_spec(args, config, W):
+    """The workload spec of ``config`` with the command line's variant options, and its tag (the
+    name of its counter summary in profiles/)."""
+    spec = W.PRESETS[config]
+    tag = config
     if args.window is not None:
         if args.window < 1:
             print("bench.py: --window must be >= 1", file=sys.stderr)
             sys.exit(2)
         sinks = spec.num_sinks if args.attn_sinks is None else args.attn_sinks
-        spec = W.preset(args.config, window=args.window, num_sinks=sinks)
-        tag = f"{args.config}_w{args.window}_s{sinks}"
+        spec = W.preset(config, window=args.window, num_sinks=sinks)
+        tag = f"{config}_w{args.window}_s{sinks}"
     elif args.attn_sinks is not None:
         print("bench.py: --attn-sinks needs --window", file=sys.stderr)
         sys.exit(2)
@@ -170,15 +223,76 @@ def main():
     if args.gamma > 1:
         spec = dataclasses.replace(spec, num_queries=args.gamma)
         tag = f"{tag}_g{args.gamma}"
+    return spec, tag
+
+
+def config_summary(line):
+    """The fields of a full bench line that the 'configs' object reports per workload."""
+    roof = line["roofline"]
+    return {
+        "workload": line["config"]["workload"],
+        "value": line["value"], "unit": line["unit"],
+        "ms_per_step": line["ms_per_step"], "us_per_step": line["us_per_step"],
+        "tokens_per_s": line["tokens_per_s"],
+        "step_frac_of_hbm_peak": line["step_frac_of_hbm_peak"],
+        "step_us_spread": line["step_us_spread"],
+        "unique_kv_bytes_per_step": line["config"]["unique_kv_bytes_per_step"],
+        "sum_ctx_len": line["config"]["sum_ctx_len"],
+        "plan": line["config"]["plan"],
+        "roofline": {k: roof[k] for k in ("bound", "kernel", "achieved", "peak", "unit", "frac",
+                                          "traffic", "traffic_over_algorithmic",
+                                          "algorithmic_bytes_per_launch", "avg_launch_us",
+                                          "launches_timed", "timed_by", "cache",
+                                          "frac_of_stream_ceiling") if k in roof},
+        "cache": line["cache"],
+        "outputs_finite": line["outputs_finite"],
+        "cpu_baseline": line["cpu_baseline"],
+    }
+
+
+def read_ceiling():
+    """The library's read probe timed on a 4 GiB buffer: the practical read ceiling."""
+    import torch
+
+    from kv_cache_decode_split_amd import kv_attn as K
+
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        K.kv_attn_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    n_probe = 10
+    a.record()
+    for _ in range(n_probe):
+        K.kv_attn_read_probe(buf, sink)
+    b.record()
+    torch.cuda.synchronize()
+    probe_us = 1e3 * a.elapsed_time(b) / n_probe
+    out = {"achieved": round(buf.numel() / (probe_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+           "bytes_per_launch": buf.numel(), "avg_launch_us": round(probe_us, 2),
+           "kernel": "kv_attn_read_probe (16-byte nontemporal loads, 1 MiB contiguous "
+                     "per workgroup, no compute)"}
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_decode(args, spec, tag, *, cpu_budget, single_thread):
+    """Passes A and B (and the append and cold-cache timings) on one workload; its bench line."""
+    import torch
+
+    from kv_cache_decode_split_amd import accounting as A
+    from kv_cache_decode_split_amd import kv_attn as K
+    from kv_cache_decode_split_amd import workloads as W
+
     layers = spec.layers
-    print(f"[bench] building {args.config} ({layers} layer(s)) on the GPU", file=sys.stderr, flush=True)
+    print(f"[bench] building {spec.name} ({layers} layer(s)) on the GPU", file=sys.stderr, flush=True)
     wls = [W.make_workload(spec, device="cuda", layer=l) for l in range(layers)]
     outs = [torch.empty(w.q.shape, dtype=torch.float32, device="cuda") for w in wls]
     # One call (and workspace) per layer, so that pass B can run all split launches before the
     # merges without one layer's split states overwriting another's.
-    if args.scores and (args.append or args.gamma > 1):
-        print("bench.py: --scores takes one query token and no --append", file=sys.stderr)
-        sys.exit(2)
     calls = [K.decode_call_for(w, o, num_splits=args.num_splits, with_scores=args.scores)
              for w, o in zip(wls, outs)]
     score_bufs = ([torch.empty((spec.batch, spec.num_kv_heads, w.max_ctx_len), dtype=torch.float32,
@@ -187,7 +301,7 @@ def main():
     elem = 2 if spec.kv_dtype == "bf16" else 4
     lens = [int(x) for x in wls[0].ctx_lens.cpu().tolist()]
     # Algorithmic bytes: the KV of the positions attended (all of them without a window).
-    gamma = args.gamma
+    gamma = max(spec.num_queries, 1)
     att = [A.attended_length(t, spec.window, spec.num_sinks, gamma) for t in lens]
     kv_bytes_layer = A.unique_kv_read_bytes(att, spec.num_kv_heads, spec.head_dim, elem)
     kv_bytes_step = kv_bytes_layer * layers
@@ -243,13 +357,14 @@ def main():
     # (kernel durations drift for ~50-100 launches, then settle), so the default warm-up covers
     # at least 0.25 s of GPU work.
     run_step = capture(step) if args.step_graph else step
-    if args.warmup is None:
+    warmup = args.warmup
+    if warmup is None:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         run_step()
         torch.cuda.synchronize()
-        args.warmup = max(5, int(0.25 / max(time.perf_counter() - t0, 1e-6)) + 1)
-    for _ in range(args.warmup):
+        warmup = max(5, int(0.25 / max(time.perf_counter() - t0, 1e-6)) + 1)
+    for _ in range(warmup):
         run_step()
     torch.cuda.synchronize()
     # An event at every step boundary: the first and last bracket the K steps (ms_per_step), the
@@ -263,28 +378,33 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
     step_us = [1e3 * marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
-    print(f"[bench] pass A done: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    print(f"[bench] {spec.name} pass A done: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
 
     # ---- cache state ------------------------------------------------------------------------------
     # Steps run back to back, so a step whose inputs fit the 256 MB last-level cache (MALL) could
     # find them there. When the bytes a step touches are under 4x that, the steps are timed once
     # more one at a time, each after writing a 512 MiB scratch buffer (outside the timed region),
-    # so that they start cold.
+    # so that they start cold; pass B below is then timed cold the same way as well.
     touched = kv_bytes_step + sum(int(w.q.numel()) * w.q.element_size() * 2 for w in wls)
-    cold_us = None
-    if touched < 4 * LLC_BYTES:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        cold_us = []
-        for _ in range(args.steps):
+    fits_cache = touched < 4 * LLC_BYTES
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if fits_cache else None
+
+    def time_cold(fn, n):
+        """Durations (µs) of ``n`` calls of ``fn``, each alone after 512 MiB of writes."""
+        out = []
+        for _ in range(n):
             scratch.fill_(7)
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
             a0.record()
-            run_step()
+            fn()
             a1.record()
             torch.cuda.synchronize()
-            cold_us.append(1e3 * a0.elapsed_time(a1))
-        del scratch
+            out.append(1e3 * a0.elapsed_time(a1))
+        return out
+
+    cold_us = time_cold(run_step, args.steps) if fits_cache else None
 
     # ---- pass B: the split kernel alone, launched back to back ------------------------------------
     # Two events bracket K rounds of split launches (each round: every layer's launch, repeated so
@@ -310,7 +430,15 @@ def main():
     torch.cuda.synchronize()
     launches_timed = args.steps * reps * len(calls)
     split_us_avg = 1e3 * a.elapsed_time(b) / launches_timed
-    print(f"[bench] pass B done: split kernel {split_us_avg:.1f} us/launch", file=sys.stderr, flush=True)
+    print(f"[bench] {spec.name} pass B done: split kernel {split_us_avg:.1f} us/launch",
+          file=sys.stderr, flush=True)
+    split_cold_us = None
+    if fits_cache:  # each layer's split launch alone, after a flush (the data is then in HBM)
+        split_cold_us = time_cold(lambda: calls[0].split(), args.steps)
+        for c in calls:
+            c.merge()
+        torch.cuda.synchronize()
+    del scratch
 
     append_info = None
     if args.append:  # the append kernel alone, launched back to back
@@ -355,36 +483,14 @@ def main():
         for _ in range(4):
             calib[1].copy_(calib[0])
         torch.cuda.synchronize()
+        del calib
 
     finite = all(bool(torch.isfinite(o).all()) for o in outs)
 
-    # ---- practical read ceiling: the library's read probe on a 4 GiB buffer ------------------------
-    stream_ceiling = None
-    if not args.no_read_probe:
-        buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(3)
-        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        for _ in range(3):
-            K.kv_attn_read_probe(buf, sink)
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        n_probe = 10
-        a.record()
-        for _ in range(n_probe):
-            K.kv_attn_read_probe(buf, sink)
-        b.record()
-        torch.cuda.synchronize()
-        probe_us = 1e3 * a.elapsed_time(b) / n_probe
-        stream_ceiling = {"achieved": round(buf.numel() / (probe_us * 1e-6) / 1e9, 1), "unit": "GB/s",
-                          "bytes_per_launch": buf.numel(), "avg_launch_us": round(probe_us, 2),
-                          "kernel": "kv_attn_read_probe (16-byte nontemporal loads, 1 MiB contiguous "
-                                    "per workgroup, no compute)"}
-        del buf, sink
-
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------------------
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wls, spec, args.cpu_seconds, elem, A)
+    if cpu_budget is not None:
+        cpu = cpu_baseline(wls, spec, cpu_budget, elem, A, single_thread=single_thread)
 
     achieved = kv_bytes_layer / (split_us_avg * 1e-6) / 1e9
     traffic, traffic_src = load_traffic(tag)
@@ -395,7 +501,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "tokens_per_s": round(A.aggregate_tokens_per_s(spec.batch * gamma, ms_per_step * 1e-3), 1),
@@ -434,13 +540,17 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / kv_bytes_layer, 4) if traffic else None,
             "algorithmic_bytes_per_launch": kv_bytes_layer,
             "avg_launch_us": round(split_us_avg, 2),
             "launches_timed": launches_timed,
             "timed_by": "host launches" if args.eager else "HIP graph replay",
-            "stream_ceiling": stream_ceiling,
-            "frac_of_stream_ceiling": (round(achieved / stream_ceiling["achieved"], 4)
-                                       if stream_ceiling else None),
+            "cache": ("streamed: the launches read far more than the 256 MB last-level cache"
+                      if split_cold_us is None else
+                      "warm: back-to-back launches re-read data that fits the 256 MB last-level "
+                      "cache; 'cold' times each launch alone after writing 512 MiB"),
+            "stream_ceiling": None,
+            "frac_of_stream_ceiling": None,
         },
         "step_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "step_us_spread": _spread(step_us),
@@ -456,6 +566,14 @@ def main():
         "cpu_baseline": cpu,
         "context": page_context(A, kv_bytes_step, ms_per_step),
     }
+    if split_cold_us is not None:
+        cold_avg = sum(split_cold_us) / len(split_cold_us)
+        cold_rate = kv_bytes_layer / (cold_avg * 1e-6) / 1e9
+        line["roofline"]["cold"] = {"avg_launch_us": round(cold_avg, 2),
+                                    "achieved": round(cold_rate, 1),
+                                    "frac": round(cold_rate / HBM_PEAK_GBPS, 4),
+                                    "launches_timed": len(split_cold_us),
+                                    "timed_by": "device events around each launch"}
     if args.scores:
         line["config"]["scores"] = ("each layer also writes every attended position's attention "
                                     "weight summed over its KV head's query heads")
@@ -466,7 +584,9 @@ def main():
         line["append"] = append_info
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
-    print(json.dumps(line), flush=True)
+    del calls, wls, outs, score_bufs, news
+    torch.cuda.empty_cache()
+    return line
 
 
 def _spread(xs):
@@ -625,7 +745,7 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wls, spec, budget_s, elem, A):
+def cpu_baseline(wls, spec, budget_s, elem, A, single_thread=True):
     """The oracle, as it stands, on whole (layer, sequence, KV head) units of the workload, in
     order, until the time budget is spent (at least one unit). Host copies of each unit are made
     outside the timed region. Returns the oracle's unique-KV GB/s on the host's BLAS threads and,
@@ -659,7 +779,7 @@ def cpu_baseline(wls, spec, budget_s, elem, A):
 
     value, sample = run(budget_s)
     out = {"value": value, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle", "sample": sample}
-    if spec.name in ("C1", "C2", "C3"):
+    if single_thread and spec.name in ("C1", "C2", "C3"):
         try:
             from threadpoolctl import threadpool_limits
         except ImportError:

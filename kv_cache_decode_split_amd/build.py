@@ -10,7 +10,9 @@ Usage: ``python -m kv_cache_decode_split_amd.build`` (or ``build()`` from Python
 from __future__ import annotations
 
 import concurrent.futures
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -32,8 +34,44 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
-HIP_SOURCES = ["kv_attn_kernels.hip", "kv_attn_api.hip", "kv_evict.hip", "kv_probe.hip"]
+# The split kernel's families compile in separate files so that the build runs them in parallel.
+HIP_SOURCES = ["kv_attn_split_vector128.hip", "kv_attn_split_vector64.hip",
+               "kv_attn_split_mfma128.hip", "kv_attn_split_mfma64.hip", "kv_attn_split_rows.hip",
+               "kv_attn_kernels.hip", "kv_attn_api.hip", "kv_evict.hip", "kv_probe.hip"]
 CXX_SOURCES = ["kv_attn_plan.cpp"]
+# hipcc's per-kernel resource report (registers, spills, scratch), checked after every compile.
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+class ScratchError(RuntimeError):
+    """A kernel of the library would spill registers to scratch memory."""
+
+
+def parse_resource_usage(text: str) -> list:
+    """The per-kernel records of hipcc's resource-usage remarks in ``text``: one dict per kernel
+    with its mangled name and the reported values (as strings) keyed by the remark's label."""
+    records = []
+    for line in text.splitlines():
+        if "remark:" not in line or RESOURCE_REMARKS not in line:
+            continue
+        body = line.split("remark:", 1)[1].rsplit("[", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            records.append({"name": body.split(":", 1)[1].strip()})
+        elif records and ":" in body:
+            key, value = body.rsplit(":", 1)
+            records[-1][key.strip()] = value.strip()
+    return records
+
+
+def scratch_offenders(records: list) -> list:
+    """Kernels that use scratch memory or spill vector registers (to scratch or to AGPRs)."""
+    bad = []
+    for r in records:
+        scratch = int(r.get("ScratchSize [bytes/lane]", "0"))
+        vspill = int(r.get("VGPRs Spill", "0"))
+        if scratch != 0 or vspill != 0:
+            bad.append(f"{r['name']}: scratch {scratch} bytes/lane, {vspill} VGPRs spilled")
+    return bad
 
 
 def _hipcc() -> str:
@@ -52,22 +90,41 @@ def _run(cmd):
     return "\n".join(lines)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source and link the library. Always rebuilds. Returns the library path."""
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every source and link the library. Always rebuilds. Returns the library path.
+
+    Fails (ScratchError) if any kernel spills registers or uses scratch memory: every kernel of
+    the library is meant to run from registers and LDS alone, and the resource report of each
+    compile is checked.
+    """
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
     cxx = os.environ.get("CXX", "g++")
+    if jobs <= 0:
+        jobs = max(1, min(8, os.cpu_count() or 1))
     steps = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        steps.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        steps.append([hipcc, *HIP_FLAGS, RESOURCE_REMARKS, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         steps.append([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    records = []
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, steps):
-            if verbose and out.strip():
-                print(out)
+            records.extend(parse_resource_usage(out))
+            # (the remarks' source excerpts are lines of the form "  123 | code" and "      | ^")
+            rest = "\n".join(l for l in out.splitlines()
+                             if RESOURCE_REMARKS not in l and not re.match(r"^\s*\d*\s*\|", l)
+                             and not l.startswith("In file included from"))
+            if verbose and rest.strip():
+                print(rest)
+    bad = scratch_offenders(records)
+    if bad:
+        raise ScratchError("kernels that spill registers:\n  " + "\n  ".join(bad))
+    with open(os.path.join(BUILD_DIR, "resource_usage.jsonl"), "w") as f:
+        for r in records:
+            f.write(json.dumps(r) + "\n")
     objs = [os.path.join(BUILD_DIR, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs])

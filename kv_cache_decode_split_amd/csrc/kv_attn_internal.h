@@ -12,10 +12,7 @@ namespace kvattn {
 constexpr int kTile = 16;
 // Waves per split workgroup; each wave streams every kWaves-th tile of the split (or, with
 // SplitArgs::wave_heads, every tile of the split for its own KV head).
-#ifndef KV_ATTN_WAVES
-#define KV_ATTN_WAVES 4
-#endif
-constexpr int kWaves = KV_ATTN_WAVES;
+constexpr int kWaves = 4;
 constexpr int kSplitThreads = 64 * kWaves;
 // Merge pass: one workgroup of kMergeThreads per (sequence, query head) row.
 constexpr int kMergeThreads = 256;
@@ -150,6 +147,14 @@ bool fault_injected(const char* where);  // KV_ATTN_FAULT=<where>: simulate a HI
 // Kernel launchers (kv_attn_kernels.hip); return a hipError_t value (0 = success).
 int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, bool q_bf16,
                  bool kv_bf16, void* stream);
+// The split kernel's instantiations, one family per file (kv_attn_split_*.hip).
+int launch_split_mfma_d64(const SplitArgs& a, const Plan& plan, bool paged, void* stream);
+int launch_split_mfma_d128(const SplitArgs& a, const Plan& plan, bool paged, void* stream);
+int launch_split_vector_d64(const SplitArgs& a, const Plan& plan, bool q_bf16, bool kv_bf16,
+                            void* stream);
+int launch_split_vector_d128(const SplitArgs& a, const Plan& plan, bool q_bf16, bool kv_bf16,
+                             void* stream);
+int launch_split_rows(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, void* stream);
 int launch_merge(const MergeArgs& a, int head_dim, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
 int launch_scores(const ScoreArgs& a, int64_t units, void* stream);

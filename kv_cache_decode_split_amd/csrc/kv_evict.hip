@@ -43,24 +43,11 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef KV_EVICT_STREAM_THREADS
-#define KV_EVICT_STREAM_THREADS 1024
-#endif
-#ifndef KV_EVICT_SLABS
-#define KV_EVICT_SLABS 4
-#endif
-#ifndef KV_EVICT_GRID
-#define KV_EVICT_GRID 256
-#endif
-#ifndef KV_EVICT_REPLICAS
-#define KV_EVICT_REPLICAS 8
-#endif
-
-constexpr int kStreamThreads = KV_EVICT_STREAM_THREADS;  // threads of a full-pass workgroup
+constexpr int kStreamThreads = 1024;                 // threads of a full-pass workgroup
 constexpr int kVec = 4;                              // floats per 128-bit load
-constexpr int kSlabs = KV_EVICT_SLABS;               // loads per thread per iteration
+constexpr int kSlabs = 4;                            // loads per thread per iteration
 constexpr int kChunk = kStreamThreads * kVec * kSlabs;  // entries per workgroup iteration
-constexpr int kGrid = KV_EVICT_GRID;                 // workgroups of the full passes (at most)
+constexpr int kGrid = 256;                           // workgroups of the full passes (at most)
 constexpr int kListGrid = 64;                        // workgroups of the list pass (at most)
 constexpr int kFinishThreads = 1024;                 // list-pass and final workgroups
 constexpr int kLdsKeys = 6144;                       // list-2 entries the final kernel stages
@@ -71,7 +58,7 @@ constexpr int kGroupBins = kBins / kGroups;
 // of one line serialise (packed, the 64 counters of a replica made pass 1 2.2x slower on MI355X).
 constexpr int kGroupStride = 32;
 constexpr int kRep = kBins + kGroups * kGroupStride; // words per replica: bins, then groups
-constexpr int kReplicas0 = KV_EVICT_REPLICAS;        // copies of the top digit's histogram
+constexpr int kReplicas0 = 8;                        // copies of the top digit's histogram
 constexpr int kReplicas1 = 4;                        // copies of the second digit's histogram
 constexpr size_t kStateBytes = 256;
 constexpr size_t kHistBytes = size_t(kReplicas0 + kReplicas1) * kRep * 4;

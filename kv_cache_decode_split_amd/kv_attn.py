@@ -43,9 +43,7 @@ __all__ = [
     "EXPORTED_SYMBOLS",
 ]
 
-# KV_ATTN_LIBRARY may name another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("KV_ATTN_LIBRARY") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libkvattn.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvattn.so")
 
 KV_ATTN_OK = 0
 KV_ATTN_ERR_NULL = 1
@@ -250,6 +248,14 @@ def _stream_handle(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _hold_for_stream(t: Optional[torch.Tensor], stream) -> None:
+    """Keep torch's caching allocator from reusing ``t`` (allocated here, on the current stream)
+    while the kernels just enqueued on ``stream`` may still use it: when ``stream`` is another
+    stream, the block is released only once that stream's work has passed this point."""
+    if t is not None and stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
 def _check_extent(t: torch.Tensor, strides, blocks: int, slots: int, heads: int, d: int, what: str):
     last = (blocks - 1) * strides[0] + (slots - 1) * strides[1] + (heads - 1) * strides[2] + d - 1
     avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
@@ -315,7 +321,10 @@ class DecodeCall:
                     else kv_attn_workspace_size(self.params))
         if with_scores and ws_bytes == 0:
             raise KvAttnError(KV_ATTN_ERR_UNSUPPORTED, "kv_attn_scores_workspace_size")
-        if ws_bytes and workspace is None:
+        # A workspace allocated here belongs to this call; one the caller passes is the caller's
+        # (who then keeps it alive until the launches that use it have finished).
+        self._own_workspace = bool(ws_bytes) and workspace is None
+        if self._own_workspace:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         if workspace is not None and workspace.device != dev:
             raise ValueError("workspace must be on q's device")
@@ -330,11 +339,16 @@ class DecodeCall:
     def plan(self) -> dict:
         return kv_attn_get_plan(self.params)
 
+    def _launched_on(self, stream) -> None:
+        if self._own_workspace:
+            _hold_for_stream(self.workspace, stream)
+
     def decode(self, stream=None) -> None:
         st = _lib.kv_attn_decode(*self._ptrs, ctypes.byref(self.params), *self._ws,
                                  _stream_handle(stream))
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode")
+        self._launched_on(stream)
 
     def decode_scores(self, token_scores: torch.Tensor, accumulate: bool = False,
                       stream=None) -> None:
@@ -350,18 +364,21 @@ class DecodeCall:
                                         ctypes.byref(self.params), *self._ws, _stream_handle(stream))
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode_scores")
+        self._launched_on(stream)
 
     def split(self, stream=None) -> None:
         st = _lib.kv_attn_decode_split(*self._ptrs, ctypes.byref(self.params), *self._ws,
                                        _stream_handle(stream))
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode_split")
+        self._launched_on(stream)
 
     def merge(self, stream=None) -> None:
         st = _lib.kv_attn_decode_merge(self._ptrs[4], self._ptrs[5], ctypes.byref(self.params),
                                        *self._ws, _stream_handle(stream))
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode_merge")
+        self._launched_on(stream)
 
     def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
         """Write each sequence's new K/V rows at positions ctx_lens[b] - gamma .. ctx_lens[b] - 1
@@ -374,6 +391,7 @@ class DecodeCall:
                                         _stream_handle(stream))
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_append_decode")
+        self._launched_on(stream)
 
 
 def _check_new_rows(k_new, v_new, cache, batch, num_kv_heads, head_dim, rows=1):

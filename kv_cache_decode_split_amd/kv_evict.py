@@ -12,7 +12,7 @@ from typing import Optional
 
 import torch
 
-from .kv_attn import _lib, _stream_handle, KvAttnError, KV_ATTN_OK
+from .kv_attn import _hold_for_stream, _lib, _stream_handle, KvAttnError, KV_ATTN_OK
 
 __all__ = ["kv_evict_params", "make_evict_params", "kv_evict_workspace_size", "kv_evict_select",
            "EXPORTED_SYMBOLS"]
@@ -75,7 +75,8 @@ def kv_evict_select(scores: torch.Tensor, budget: int, current: Optional[int] = 
         avail = scores.untyped_storage().nbytes() // 4 - scores.storage_offset()
         if last > avail:
             raise ValueError("scores view extends past its storage")
-    if keep is None:
+    own_keep = keep is None
+    if own_keep:
         keep = torch.empty((L, H, N), dtype=torch.uint8, device=scores.device)
     elif keep.shape != (L, H, N) or keep.dtype != torch.uint8 or not keep.is_contiguous() \
             or keep.device != scores.device:
@@ -85,7 +86,8 @@ def kv_evict_select(scores: torch.Tensor, budget: int, current: Optional[int] = 
                                      or kept_per_row.device != scores.device):
         raise ValueError("kept_per_row must be a contiguous int32 [L, H] tensor on the scores' device")
     need = kv_evict_workspace_size(p)
-    if need and workspace is None:
+    own_workspace = bool(need) and workspace is None
+    if own_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -94,4 +96,9 @@ def kv_evict_select(scores: torch.Tensor, budget: int, current: Optional[int] = 
                               ctypes.byref(p), ws_ptr, ws_bytes, _stream_handle(stream))
     if st != KV_ATTN_OK:
         raise KvAttnError(st, "kv_evict_select")
+    # Buffers allocated here on the current stream must outlive the launches on `stream`.
+    if own_workspace:
+        _hold_for_stream(workspace, stream)
+    if own_keep:
+        _hold_for_stream(keep, stream)
     return keep

@@ -20,6 +20,8 @@ HEADER = os.path.join(ROOT, "include", "kv_attn.h")
 K = pytest.importorskip("kv_cache_decode_split_amd.kv_attn",
                         reason="libkvattn.so not built (run python -m kv_cache_decode_split_amd.build)")
 
+from tests import plan_cases as C  # noqa: E402
+
 
 def _declared_functions():
     text = open(HEADER).read()
@@ -70,33 +72,15 @@ def test_abi_version_and_status_strings():
 
 
 def _params(**kw):
-    base = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
-                max_ctx_len=1000, num_blocks=300, k_strides=(8 * 16 * 128, 128, 16 * 128),
-                v_strides=(8 * 16 * 128, 128, 16 * 128), max_blocks_per_seq=63)
-    base.update(kw)
-    return K.make_params(**base)
+    return K.make_params(**C.params_kwargs(**kw))
 
 
-@pytest.mark.parametrize("kw,status", [
-    (dict(batch=0), K.KV_ATTN_ERR_SHAPE),
-    (dict(num_q_heads=30), K.KV_ATTN_ERR_SHAPE),            # not a multiple of h_kv
-    (dict(num_q_heads=8 * 17), K.KV_ATTN_ERR_UNSUPPORTED),  # group 17 > 16
-    (dict(batch=1 << 24, num_queries=2), K.KV_ATTN_ERR_UNSUPPORTED),  # 2^31 append pieces
-    (dict(head_dim=96), K.KV_ATTN_ERR_UNSUPPORTED),
-    (dict(q_dtype=5), K.KV_ATTN_ERR_UNSUPPORTED),
-    (dict(k_strides=(8 * 16 * 128, 127, 16 * 128)), K.KV_ATTN_ERR_UNSUPPORTED),  # misaligned rows
-    (dict(v_strides=(-1, 128, 16 * 128)), K.KV_ATTN_ERR_SHAPE),
-    (dict(max_ctx_len=-1), K.KV_ATTN_ERR_VALUE),
-    (dict(num_splits=-2), K.KV_ATTN_ERR_VALUE),
-    (dict(scale=float("nan")), K.KV_ATTN_ERR_VALUE),
-    (dict(num_blocks=0), K.KV_ATTN_ERR_SHAPE),
-    (dict(window=64, num_sinks=-1), K.KV_ATTN_ERR_VALUE),
-])
+@pytest.mark.parametrize("kw,status", C.INVALID_PARAM_CASES)
 def test_get_plan_rejects_invalid_params(kw, status):
     p = _params(**kw)
     with pytest.raises(K.KvAttnError) as e:
         K.kv_attn_get_plan(p, 256)
-    assert e.value.status == status
+    assert e.value.status == getattr(K, status)
 
 
 @pytest.mark.parametrize("field,value", [("window", -1), ("num_queries", -1)])
@@ -204,22 +188,9 @@ def test_random_plans_cover_the_visited_tiles_within_the_bounds():
     """Seeded sweep over shapes, windows, query tokens and CU counts: the splits cover exactly
     the tiles a sequence can visit, within the split-length bounds, and the workspace holds
     every split state."""
-    rnd = np.random.default_rng(17)
-    for _ in range(400):
-        B = int(rnd.integers(1, 200))
-        hkv = int(rnd.choice([1, 2, 4, 8, 32]))
-        g = int(rnd.choice([1, 2, 3, 4, 8, 16]))
-        nq = int(rnd.choice([1, 1, 2, 4]))
-        if nq * g > 32:
-            nq = 1
-        T = int(rnd.choice([1, 15, 16, 17, 300, 4096, 8191, 32768, 131072, 1 << 20]))
-        W = int(rnd.choice([0, 0, 1, 64, 1000, 4096]))
-        n = int(rnd.choice([0, 4, 100]))
-        cus = int(rnd.choice([1, 64, 256, 304]))
-        p = _params(batch=B, num_q_heads=hkv * g, num_kv_heads=hkv, max_ctx_len=T,
-                    max_blocks_per_seq=(T + 15) // 16, num_blocks=10**7, window=W or None, num_sinks=n,
-                    num_queries=nq)
-        plan = K.kv_attn_get_plan(p, cus)
+    for kw, cus, c in C.random_plan_cases():
+        B, hkv, g, nq, T, W, n = (c[k] for k in ("B", "hkv", "g", "nq", "T", "W", "n"))
+        plan = K.kv_attn_get_plan(K.make_params(**kw), cus)
         all_tiles = (T + 15) // 16
         bound = all_tiles if W == 0 else min(all_tiles, (min(n, T) + 15) // 16
                                               + (W + nq - 1 + 15) // 16 + 1)
@@ -258,8 +229,7 @@ def test_plan_for_the_five_workloads():
         assert plan["kernel_variant"] == (2 if hq // hkv >= 4 else 1)
 
 
-def _token_major(hkv, d=128, bs=16):
-    return dict(k_strides=(bs * hkv * d, hkv * d, d), v_strides=(bs * hkv * d, hkv * d, d))
+_token_major = C.token_major
 
 
 def test_token_major_plan_gives_each_wave_its_own_kv_head():
@@ -310,18 +280,9 @@ def test_token_major_plan_gives_each_wave_its_own_kv_head():
 
 
 def test_random_token_major_plans_cover_the_tiles():
-    rnd = np.random.default_rng(23)
-    for _ in range(300):
-        B = int(rnd.integers(1, 200))
-        hkv = int(rnd.choice([4, 8, 12, 32]))
-        g = int(rnd.choice([1, 2, 4, 8]))
-        T = int(rnd.choice([1, 15, 17, 300, 4096, 32768, 131072, 1 << 20]))
-        W = int(rnd.choice([0, 0, 64, 4096]))
-        cus = int(rnd.choice([1, 64, 256, 304]))
-        p = _params(batch=B, num_q_heads=hkv * g, num_kv_heads=hkv, max_ctx_len=T,
-                    max_blocks_per_seq=(T + 15) // 16, num_blocks=10**7, window=W or None,
-                    num_sinks=4, **_token_major(hkv))
-        plan = K.kv_attn_get_plan(p, cus)
+    for kw, cus, c in C.random_token_major_cases():
+        B, hkv, g, T, W = (c[k] for k in ("B", "hkv", "g", "T", "W"))
+        plan = K.kv_attn_get_plan(K.make_params(**kw), cus)
         all_tiles = (T + 15) // 16
         bound = all_tiles if W == 0 else min(all_tiles, 1 + (W + 15) // 16 + 1)
         S, L = plan["num_splits"], plan["split_len"]
@@ -371,9 +332,8 @@ def test_decode_null_pointers_fail_before_any_hip_call():
 
 
 def test_decode_layout_errors_fail_before_any_hip_call():
-    assert _decode_raw(_params(block_size=24)) == K.KV_ATTN_ERR_SHAPE            # not a power of 2
-    assert _decode_raw(_params(block_size=8, max_blocks_per_seq=200)) == K.KV_ATTN_ERR_SHAPE
-    assert _decode_raw(_params(max_ctx_len=63 * 16 + 1)) == K.KV_ATTN_ERR_SHAPE  # exceeds the table
+    for kw in C.INVALID_LAYOUT_CASES:
+        assert _decode_raw(_params(**kw)) == K.KV_ATTN_ERR_SHAPE, kw
     assert _decode_raw(_params(block_size=500), bt=None) == K.KV_ATTN_ERR_SHAPE  # capacity < max ctx
     assert _decode_raw(_params(block_size=1000, num_blocks=3), bt=None) == K.KV_ATTN_ERR_SHAPE
     assert _decode_raw(_params(), q=8) == K.KV_ATTN_ERR_UNSUPPORTED              # misaligned
