@@ -173,15 +173,20 @@ def main():
             print(f"bench.py: --also names an unknown workload {c!r}", file=sys.stderr)
             sys.exit(2)
 
-    line = measure_decode(args, spec, tag, cpu_budget=None if args.no_cpu_baseline else args.cpu_seconds,
-                          single_thread=True)
+    # Every GPU timing runs back to back (the device slows down for a while after sitting idle,
+    # e.g. during a CPU-baseline leg), and the CPU baselines follow once they are all done.
+    line, main_inputs = measure_decode(args, spec, tag)
     ceiling = None if args.no_read_probe else read_ceiling()
-    extras = {}
+    extras, extra_inputs = {}, {}
     for c in also:
         extra_spec, extra_tag = resolve_spec(args, c, W)
-        extras[c] = measure_decode(args, extra_spec, extra_tag,
-                                   cpu_budget=None if args.no_cpu_baseline else args.also_cpu_seconds,
-                                   single_thread=False)
+        extras[c], extra_inputs[c] = measure_decode(args, extra_spec, extra_tag)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(*main_inputs, args.cpu_seconds, single_thread=True)
+        for c in also:
+            extras[c]["cpu_baseline"] = cpu_baseline(*extra_inputs[c], args.also_cpu_seconds,
+                                                     single_thread=False)
+    del main_inputs, extra_inputs
     for ln in [line, *extras.values()]:
         roof = ln["roofline"]
         roof["stream_ceiling"] = ceiling
@@ -279,8 +284,10 @@ def read_ceiling():
     return out
 
 
-def measure_decode(args, spec, tag, *, cpu_budget, single_thread):
-    """Passes A and B (and the append and cold-cache timings) on one workload; its bench line."""
+def measure_decode(args, spec, tag):
+    """Passes A and B (and the append and cold-cache timings) on one workload: its bench line
+    (cpu_baseline still None) and the inputs the CPU baseline needs (the workload, kept on the
+    device)."""
     import torch
 
     from kv_cache_decode_split_amd import accounting as A
@@ -487,11 +494,6 @@ def measure_decode(args, spec, tag, *, cpu_budget, single_thread):
 
     finite = all(bool(torch.isfinite(o).all()) for o in outs)
 
-    # ---- CPU baseline: the oracle on a bounded sample --------------------------------------------
-    cpu = None
-    if cpu_budget is not None:
-        cpu = cpu_baseline(wls, spec, cpu_budget, elem, A, single_thread=single_thread)
-
     achieved = kv_bytes_layer / (split_us_avg * 1e-6) / 1e9
     traffic, traffic_src = load_traffic(tag)
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -563,7 +565,7 @@ def measure_decode(args, spec, tag, *, cpu_budget, single_thread):
             "cold_us_per_step": _spread(cold_us) if cold_us else None,
         },
         "outputs_finite": finite,
-        "cpu_baseline": cpu,
+        "cpu_baseline": None,
         "context": page_context(A, kv_bytes_step, ms_per_step),
     }
     if split_cold_us is not None:
@@ -584,9 +586,9 @@ def measure_decode(args, spec, tag, *, cpu_budget, single_thread):
         line["append"] = append_info
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
-    del calls, wls, outs, score_bufs, news
+    del calls, outs, score_bufs, news
     torch.cuda.empty_cache()
-    return line
+    return line, (wls, spec, elem)
 
 
 def _spread(xs):
@@ -745,11 +747,12 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wls, spec, budget_s, elem, A, single_thread=True):
+def cpu_baseline(wls, spec, elem, budget_s, single_thread=True):
     """The oracle, as it stands, on whole (layer, sequence, KV head) units of the workload, in
     order, until the time budget is spent (at least one unit). Host copies of each unit are made
     outside the timed region. Returns the oracle's unique-KV GB/s on the host's BLAS threads and,
     for C1-C3, also on one thread (a third of the budget)."""
+    from kv_cache_decode_split_amd import accounting as A
     from kv_cache_decode_split_amd import workloads as W
     from oracle import decode_attention, verify_attention
 
