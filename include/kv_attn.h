@@ -27,8 +27,9 @@
  * - Every argument the host can see is validated before any HIP call; on an invalid argument
  *   nothing is launched and the status says why. Contents of device-resident arrays (ctx_lens,
  *   block_table) are not validated on the fast path; see kv_attn_validate_host.
- * - Entry points are thread-safe: the only shared state is a per-device cache of the compute
- *   unit count, filled once.
+ * - Entry points are thread-safe: the only shared host state is a per-device cache of the
+ *   compute unit count and one of the address of kv_attn_decode_noalloc's device scratch, each
+ *   filled once (that scratch itself is shared by the calls on a device, see there).
  * - GQA grouping: with g = num_q_heads / num_kv_heads, query head h reads KV head h / g.
  * - ctx_lens[b] counts every position in the cache, the current token included (the caller has
  *   already appended it). Without a window every one of them is attended; ctx_lens[b] == 0
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KV_ATTN_ABI_VERSION 3
+#define KV_ATTN_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum kv_attn_status {
@@ -71,7 +72,9 @@ typedef enum kv_attn_status {
   KV_ATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the plan needs */
   KV_ATTN_ERR_HIP = 5,         /* the HIP runtime reported an error (launch or query) */
   KV_ATTN_ERR_TABLE = 6,       /* validator: ctx_lens / block_table content out of range */
-  KV_ATTN_ERR_VALUE = 7        /* an invalid scalar (non-finite scale, negative count) */
+  KV_ATTN_ERR_VALUE = 7,       /* an invalid scalar (non-finite scale, negative count) */
+  KV_ATTN_ERR_SCRATCH = 8      /* kv_attn_decode_noalloc: the plan needs more workspace than
+                                  the library's fixed device scratch holds */
 } kv_attn_status;
 
 /* Storage types of q and of the KV cache. */
@@ -323,6 +326,25 @@ kv_attn_status kv_attn_decode_scores(const void* q, const void* k_cache, const v
  */
 kv_attn_status kv_attn_validate_host(const int32_t* block_table, const int32_t* ctx_lens,
                                      const kv_attn_params* p);
+
+/*
+ * kv_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, checks and results as
+ * kv_attn_decode (the same plan and kernels, so the output is bit-identical to it), but the
+ * split states go to a device array the library holds itself, KV_ATTN_NOALLOC_SCRATCH_BYTES
+ * bytes per device, kept until the process ends. Nothing is allocated or freed by the call.
+ * Returns KV_ATTN_ERR_SCRATCH, before anything is launched, when the plan needs a larger
+ * workspace than that (kv_attn_workspace_size(p) > KV_ATTN_NOALLOC_SCRATCH_BYTES). Every call
+ * on a device uses that device's one array: calls that overlap on one device (other streams,
+ * other threads, other graphs in flight) race on it and must be serialised by the caller. Its
+ * contents need no initialisation (each call writes every state it reads) and are left
+ * unspecified. The first call on a device looks up the array's address there (HIP error:
+ * KV_ATTN_ERR_HIP); graph capture therefore works from the second call on a device.
+ */
+#define KV_ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+kv_attn_status kv_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      float* out, const kv_attn_params* p, void* stream);
 
 /*
  * Measurement aid, not part of attention: the practical read ceiling of the device. Streams

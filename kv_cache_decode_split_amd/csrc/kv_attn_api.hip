@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "kv_attn_internal.h"
@@ -59,6 +60,29 @@ kv_attn_status debug_validate(const int32_t* block_table, const int32_t* ctx_len
       return KV_ATTN_ERR_HIP;
   }
   return kv_attn_validate_host(block_table != nullptr ? table.data() : nullptr, ctx.data(), p);
+}
+
+// Device scratch of kv_attn_decode_noalloc: one copy per device, held until the process ends.
+// Host code never uses the array's name as an address; it uses the per-device pointer that
+// hipGetSymbolAddress returns for the device that is current.
+static __device__ __align__(256) unsigned char scratch[KV_ATTN_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // nullptr = not looked up yet on that device
+std::mutex g_scratch_mutex;
+
+// Address of the current device's copy of `scratch` (looked up once per device), or nullptr on
+// a HIP error.
+void* scratch_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
 }
 
 }  // namespace
@@ -382,6 +406,31 @@ kv_attn_status kv_attn_decode_scores(const void* q, const void* k_cache, const v
   return kvattn::decode_impl(kvattn::kPassSplit | kvattn::kPassMerge, q, k_cache, v_cache,
                              block_table, ctx_lens, out, p, workspace, workspace_bytes, stream,
                              nullptr, nullptr, token_scores, accumulate);
+}
+
+kv_attn_status kv_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* ctx_lens,
+                                      float* out, const kv_attn_params* p, void* stream) {
+  using namespace kvattn;
+  // The host-side checks of kv_attn_decode come first (decode_impl repeats them, unchanged).
+  if (p == nullptr || ctx_lens == nullptr || out == nullptr || q == nullptr || k_cache == nullptr ||
+      v_cache == nullptr)
+    return KV_ATTN_ERR_NULL;
+  kv_attn_status st = validate_layout(p, block_table != nullptr);
+  if (st != KV_ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return KV_ATTN_ERR_UNSUPPORTED;
+  if (fault_injected("query")) return KV_ATTN_ERR_HIP;
+  const int cus = current_cu_count();
+  if (cus <= 0) return KV_ATTN_ERR_HIP;
+  Plan plan;
+  st = make_plan(p, cus, &plan);
+  if (st != KV_ATTN_OK) return st;
+  if (plan.workspace_bytes > uint64_t(KV_ATTN_NOALLOC_SCRATCH_BYTES)) return KV_ATTN_ERR_SCRATCH;
+  void* ws = plan.num_splits > 1 ? scratch_for_current_device() : nullptr;
+  if (plan.num_splits > 1 && ws == nullptr) return KV_ATTN_ERR_HIP;
+  return decode_impl(kPassSplit | kPassMerge, q, k_cache, v_cache, block_table, ctx_lens, out, p,
+                     ws, ws != nullptr ? size_t(KV_ATTN_NOALLOC_SCRATCH_BYTES) : 0, stream);
 }
 
 kv_attn_status kv_attn_merge(const float* o_partial, const float* ml_partial,

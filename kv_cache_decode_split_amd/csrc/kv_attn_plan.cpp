@@ -226,6 +226,7 @@ const char* kv_attn_status_string(int32_t status) {
     case KV_ATTN_ERR_HIP: return "HIP runtime error";
     case KV_ATTN_ERR_TABLE: return "ctx_lens or block_table content out of range";
     case KV_ATTN_ERR_VALUE: return "invalid scalar argument";
+    case KV_ATTN_ERR_SCRATCH: return "problem needs more workspace than the fixed device scratch";
     default: return "unknown status";
   }
 }

@@ -38,8 +38,10 @@ __all__ = [
     "kv_attn_validate_host",
     "kv_attn_scores_workspace_size",
     "kv_attn_decode_scores",
+    "kv_attn_decode_noalloc",
     "kv_attn_read_probe",
     "KV_ATTN_PROBE_CHUNK",
+    "KV_ATTN_NOALLOC_SCRATCH_BYTES",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -53,6 +55,7 @@ KV_ATTN_ERR_WORKSPACE = 4
 KV_ATTN_ERR_HIP = 5
 KV_ATTN_ERR_TABLE = 6
 KV_ATTN_ERR_VALUE = 7
+KV_ATTN_ERR_SCRATCH = 8
 
 KV_ATTN_F32 = 0
 KV_ATTN_BF16 = 1
@@ -71,10 +74,12 @@ EXPORTED_SYMBOLS = (
     "kv_attn_validate_host",
     "kv_attn_scores_workspace_size",
     "kv_attn_decode_scores",
+    "kv_attn_decode_noalloc",
     "kv_attn_read_probe",
 )
 
 KV_ATTN_PROBE_CHUNK = 1 << 20
+KV_ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KvAttnError(RuntimeError):
@@ -158,6 +163,8 @@ def _load():
     lib.kv_attn_decode_scores.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                           P(kv_attn_params), vp, ctypes.c_size_t, vp]
     lib.kv_attn_decode_scores.restype = ctypes.c_int
+    lib.kv_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, P(kv_attn_params), vp]
+    lib.kv_attn_decode_noalloc.restype = ctypes.c_int
     lib.kv_attn_read_probe.argtypes = [vp, ctypes.c_uint64, vp, vp]
     lib.kv_attn_read_probe.restype = ctypes.c_int
     return lib
@@ -281,7 +288,8 @@ class DecodeCall:
                  k_strides: Sequence[int], v_strides: Sequence[int], block_size: int,
                  num_blocks: int, max_ctx_len: Optional[int] = None, scale: float = 0.0,
                  num_splits: int = 0, workspace: Optional[torch.Tensor] = None,
-                 window: Optional[int] = None, num_sinks: int = 0, with_scores: bool = False):
+                 window: Optional[int] = None, num_sinks: int = 0, with_scores: bool = False,
+                 allocate_workspace: bool = True):
         if q.dim() not in (3, 4) or not q.is_contiguous():
             raise ValueError("q must be a contiguous [B, h_q, d] or [B, gamma, h_q, d] tensor")
         B, hq, d = q.shape[0], q.shape[-2], q.shape[-1]
@@ -323,7 +331,7 @@ class DecodeCall:
             raise KvAttnError(KV_ATTN_ERR_UNSUPPORTED, "kv_attn_scores_workspace_size")
         # A workspace allocated here belongs to this call; one the caller passes is the caller's
         # (who then keeps it alive until the launches that use it have finished).
-        self._own_workspace = bool(ws_bytes) and workspace is None
+        self._own_workspace = bool(ws_bytes) and workspace is None and allocate_workspace
         if self._own_workspace:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         if workspace is not None and workspace.device != dev:
@@ -349,6 +357,14 @@ class DecodeCall:
         if st != KV_ATTN_OK:
             raise KvAttnError(st, "kv_attn_decode")
         self._launched_on(stream)
+
+    def decode_noalloc(self, stream=None) -> None:
+        """kv_attn_decode_noalloc: the split states go to the library's own device scratch
+        (nothing is allocated; calls that overlap on one device race on that scratch)."""
+        st = _lib.kv_attn_decode_noalloc(*self._ptrs, ctypes.byref(self.params),
+                                         _stream_handle(stream))
+        if st != KV_ATTN_OK:
+            raise KvAttnError(st, "kv_attn_decode_noalloc")
 
     def decode_scores(self, token_scores: torch.Tensor, accumulate: bool = False,
                       stream=None) -> None:
@@ -406,6 +422,14 @@ def _check_new_rows(k_new, v_new, cache, batch, num_kv_heads, head_dim, rows=1):
 def kv_attn_decode(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None, **kwargs) -> None:
     """Enqueue one decode-attention step (both passes); arguments as for :class:`DecodeCall`."""
     DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, **kwargs).decode(stream)
+
+
+def kv_attn_decode_noalloc(q, k_cache, v_cache, block_table, ctx_lens, out, *, stream=None,
+                           **kwargs) -> None:
+    """One decode step with no device allocation at all (the library's fixed scratch holds the
+    split states); arguments as for :class:`DecodeCall` (no workspace)."""
+    DecodeCall(q, k_cache, v_cache, block_table, ctx_lens, out, allocate_workspace=False,
+               **kwargs).decode_noalloc(stream)
 
 
 def kv_attn_scores_workspace_size(params: kv_attn_params) -> int:

@@ -64,8 +64,8 @@ def test_struct_layout_matches_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert K.kv_attn_abi_version() == 3
-    for code in range(8):
+    assert K.kv_attn_abi_version() == 4
+    for code in range(9):
         s = K.kv_attn_status_string(code)
         assert s and s != "unknown status"
     assert K.kv_attn_status_string(99) == "unknown status"
