@@ -722,7 +722,7 @@ def bench_evict(args, W):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "kv_evict_select (whole call: init, two streaming passes, list passes, patch)",
+            "kernel": "kv_evict_select (whole call: init sample, one streaming pass, list pass, final)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -14,9 +14,12 @@
  *      set is unique.
  * The page ranks the pool with one global sort. Here the same set comes from a radix selection
  * of the (M - L*H)-th largest 64-bit key (score bits made order-preserving, then the complement
- * of the flat index (l*H + h)*N + t, so that ties fall to the lower index): two streaming passes
- * over the scores (a histogram of the top digit; then the mask, with the entries of the
- * boundary digit set aside), then passes over the set-aside entries only.
+ * of the flat index (l*H + h)*N + t, so that ties fall to the lower index): a sample of the
+ * scores places a narrow band of key values around that key, one streaming pass over the scores
+ * writes the mask outside the band and sets the band's entries aside while counting exactly,
+ * and passes over the set-aside entries finish the selection. Should the exact counts show that
+ * the selected key lies outside the band (a sample unlike the rest of the scores), one workgroup
+ * computes the whole selection exactly instead: the result is the same, only slower.
  *
  * Readings where the page is silent: scores compare as values (-0.0 ties with +0.0, +-inf are
  * allowed, NaN is outside the contract); C is one position shared by every row; when
@@ -46,7 +49,7 @@ typedef struct kv_evict_params {
 
 /*
  * Workspace bytes kv_evict_select needs for `p`: 0 when the budget alone decides the result
- * (M - L*H <= 0, or M - L*H >= L*H*(N - 1)), otherwise 495872 bytes of selection state and
+ * (M - L*H <= 0, or M - L*H >= L*H*(N - 1)), otherwise 930048 bytes of selection state and
  * histograms plus two candidate lists of 8 bytes per slot, each with at least L*H*N slots
  * (rounded up to whole blocks of 16384 entries per workgroup). Returns 0 for invalid `p`.
  */
@@ -72,6 +75,8 @@ size_t kv_evict_workspace_size(const kv_evict_params* p);
  * range, row_stride < N), KV_ATTN_ERR_VALUE (budget < 0), KV_ATTN_ERR_UNSUPPORTED (L*H*N >=
  * 2^31, misaligned pointers), KV_ATTN_ERR_WORKSPACE, all before anything is launched, or
  * KV_ATTN_ERR_HIP if a launch fails.
+ * Environment: KV_EVICT_FORCE_FALLBACK=1 (read at each call; a test aid) sends every ranked call
+ * down the exact single-workgroup path; the mask is the same.
  */
 kv_attn_status kv_evict_select(const float* scores, uint8_t* keep, int32_t* kept_per_row,
                                const kv_evict_params* p, void* workspace, size_t workspace_bytes,

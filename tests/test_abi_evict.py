@@ -47,7 +47,7 @@ def test_params_layout_matches_the_header():
 
 
 def test_workspace_size_follows_the_budget():
-    fixed = 495872
+    fixed = 930048
     for L, H, N in [(2, 3, 10), (32, 32, 4096), (32, 8, 131072), (3, 5, 777)]:
         n, pool = L * H * N, L * H * (N - 1)
         for M in (0, L * H, L * H + pool, 10**12):  # the budget alone decides

@@ -202,3 +202,34 @@ def test_selection_over_a_billion_entries():
     finally:
         del scores, keep
         torch.cuda.empty_cache()
+
+
+FALLBACK = [
+    (4, 8, 300, "lognormal", 0.3, 299, None),
+    (4, 8, 5000, "levels", 0.1, 17, None),
+    (3, 5, 4097, "normal", 0.5, 100, 4100),     # strided rows
+    (8, 8, 4096, "lognormal", 0.25, 4095, None),  # sampled in chunks (above 131072 entries)
+]
+
+
+@pytest.mark.parametrize("case", FALLBACK, ids=[f"fb{i}" for i in range(len(FALLBACK))])
+def test_exact_fallback_matches_oracle(case, monkeypatch):
+    """The exact path the final workgroup takes when k* lies outside the sampled band (forced
+    here for every ranked call) gives the same mask."""
+    E = _evict()
+    L, H, N, kind, frac, current, stride = case
+    monkeypatch.setenv("KV_EVICT_FORCE_FALLBACK", "1")
+    scores = W.make_scores(L, H, N, kind, seed=N + L, device="cuda", row_stride=stride)
+    _run_case(E, scores, int(frac * L * H * N), current, f"fallback {kind}")
+
+
+def test_sample_unlike_the_rest_still_selects_exactly():
+    """Scores whose sampled region differs from the rest (the first 1/64 of every row is large,
+    the sampled chunks lie all over the array): the band may miss k*, and the result must still
+    be the exact selection."""
+    E = _evict()
+    L, H, N = 8, 8, 8192
+    scores = W.make_scores(L, H, N, "lognormal", seed=91, device="cuda")
+    scores[:, :, : N // 64] += 1000.0
+    for frac in (0.01, 0.1, 0.5):
+        _run_case(E, scores, int(frac * L * H * N), N - 1, f"skewed {frac}")
