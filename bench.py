@@ -175,12 +175,14 @@ def main():
 
     # Every GPU timing runs back to back (the device slows down for a while after sitting idle,
     # e.g. during a CPU-baseline leg), and the CPU baselines follow once they are all done.
+    # The read probe runs after every workload: timed right after it frees its 4 GiB buffer, C3's
+    # split kernel ran 318 instead of 307 us per launch.
     line, main_inputs = measure_decode(args, spec, tag)
-    ceiling = None if args.no_read_probe else read_ceiling()
     extras, extra_inputs = {}, {}
     for c in also:
         extra_spec, extra_tag = resolve_spec(args, c, W)
         extras[c], extra_inputs[c] = measure_decode(args, extra_spec, extra_tag)
+    ceiling = None if args.no_read_probe else read_ceiling()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(*main_inputs, args.cpu_seconds, single_thread=True)
         for c in also:

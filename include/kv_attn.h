@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KV_ATTN_ABI_VERSION 4
+#define KV_ATTN_ABI_VERSION 5
 
 /* Status codes. */
 typedef enum kv_attn_status {
@@ -156,8 +156,22 @@ typedef struct kv_attn_plan {
                                The automatic S then counts batch * num_kv_heads / 4 workgroups
                                per split and allows one split per 4 tiles. 0: one KV head per
                                workgroup. */
+  int32_t unit_order;       /* 1: a one-workgroup order kernel first lists the (sequence, split)
+                               pairs longest first (whole splits, then the sequences' last
+                               partial splits by decreasing length; empty pairs last, as -1,
+                               their workgroups leaving at once) and the split workgroups take
+                               them in that order, so the last workgroups dispatched are the
+                               shortest (on MI355X, C4's ragged batch: split kernel 1397 ->
+                               1334 us). Chosen when S > 1, S <= 256, no halves
+                               and batch * num_kv_heads (/ 4 with wave_heads) >= 4 * num_cus,
+                               i.e. the split workgroups take several rounds of the device.
+                               Not used by kv_attn_decode_scores. 0: workgroups take the pairs
+                               split by split. */
+  int32_t reserved;         /* 0 */
   uint64_t workspace_bytes; /* workspace kv_attn_decode needs (0 when S == 1) */
   uint64_t ml_offset;       /* byte offset of the (m, l) array inside the workspace (S > 1) */
+  uint64_t order_offset;    /* byte offset of the order list (batch * S int32) inside the
+                               workspace when unit_order, else 0 */
 } kv_attn_plan;
 
 /* ABI version of the loaded library (KV_ATTN_ABI_VERSION it was built with). */

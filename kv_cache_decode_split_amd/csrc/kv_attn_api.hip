@@ -112,8 +112,11 @@ kv_attn_status kv_attn_get_plan(const kv_attn_params* p, int32_t num_cus, kv_att
   plan->group_padded = pl.group_padded;
   plan->num_cus = cus;
   plan->wave_heads = pl.wave_heads;
+  plan->unit_order = pl.unit_order;
+  plan->reserved = 0;
   plan->workspace_bytes = pl.workspace_bytes;
   plan->ml_offset = pl.num_splits > 1 ? pl.o_part_bytes : 0;
+  plan->order_offset = pl.unit_order ? pl.order_bytes_offset : 0;
   return KV_ATTN_OK;
 }
 
@@ -284,6 +287,22 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.row_stats = plan.num_splits == 1 ? row_stats : nullptr;
     const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
     a.scale_log2 = float(scale * 1.4426950408889634);  // log2(e)
+    a.order = nullptr;
+    if (plan.unit_order && !scores) {  // the score export keeps the split-by-split order
+      int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_bytes_offset);
+      OrderArgs oa;
+      oa.ctx_lens = ctx_lens;
+      oa.order = order;
+      oa.batch = p->batch;
+      oa.num_splits = plan.num_splits;
+      oa.split_tiles = plan.split_tiles;
+      oa.max_ctx = p->max_ctx_len;
+      oa.window = p->window;
+      oa.num_sinks = p->num_sinks;
+      oa.num_queries = plan.num_queries;
+      if (launch_order(oa, stream) != 0) return KV_ATTN_ERR_HIP;
+      a.order = order;
+    }
     if (launch_split(a, plan, p->head_dim, paged, p->q_dtype == KV_ATTN_BF16,
                      p->kv_dtype == KV_ATTN_BF16, stream) != 0)
       return KV_ATTN_ERR_HIP;

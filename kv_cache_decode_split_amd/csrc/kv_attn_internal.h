@@ -26,6 +26,11 @@ constexpr int kMaxQueries = 16;
 constexpr int kRowsMinGroup = 4;      // one query token: rows mode from this group size on (bf16)
 constexpr int kVectorMaxGroup = 8;    // vector path: query heads one workgroup holds
 constexpr int kWaveHeadsMinTiles = 32; // wave heads: tiles per wave, at least, on a full device
+constexpr int kOrderMaxSplits = 256;   // unit order: splits per sequence, at most (one lane
+                                       // of a wave scans 4 counters each)
+constexpr int kOrderThreads = 256;    // unit order: the order kernel's one workgroup
+constexpr int kOrderMinRounds = 4;     // unit order: split workgroups per split / CUs, at least
+constexpr int kOrderBuckets = 256;     // unit order: partial-split lengths are ranked in 256 classes
 
 // Everything the split kernel needs, by value.
 struct SplitArgs {
@@ -61,6 +66,23 @@ struct SplitArgs {
                                // position (one query token per sequence only)
   int64_t logits_ld;           // multiple of kTile, >= max_ctx rounded up to kTile
   float* row_stats;            // nullptr, or [B * h_q, 2]: final (m, l) per row (num_splits == 1)
+  const int32_t* order;        // nullptr, or [B * S]: entry i = b * S + split of the i-th
+                               // (sequence, split) pair to serve, or -1 for an empty pair
+                               // (head_chunks == 1); its workgroups are the next
+                               // units-per-split indices
+};
+
+// The order kernel: a permutation of the B * S (sequence, split) pairs, longest first.
+struct OrderArgs {
+  const int32_t* ctx_lens;
+  int32_t* order;              // [B * S]: the non-empty pairs longest first, then -1 each
+  int32_t batch;
+  int32_t num_splits;          // S <= kOrderMaxSplits
+  int32_t split_tiles;
+  int32_t max_ctx;
+  int32_t window;
+  int32_t num_sinks;
+  int32_t num_queries;
 };
 
 struct MergeArgs {
@@ -130,10 +152,12 @@ struct Plan {
   int32_t row_blocks;   // rows mode: blocks of 16 query rows per (sequence, KV head)
   int32_t head_chunks;  // vector path: the group's query heads served by this many workgroups
   int32_t wave_heads;   // 1: each wave of a split workgroup serves its own KV head (SplitArgs)
+  int32_t unit_order;   // 1: the order kernel lists the (sequence, split) pairs longest first
   int64_t grid_split;
   int64_t grid_merge;
   uint64_t workspace_bytes;
   uint64_t o_part_bytes;  // offset of ml_part inside the workspace
+  uint64_t order_bytes_offset;  // offset of the order list (batch * S int32) when unit_order
 };
 
 // Host-only helpers (kv_attn_plan.cpp; no HIP calls).
@@ -156,6 +180,7 @@ int launch_split_vector_d128(const SplitArgs& a, const Plan& plan, bool q_bf16, 
                              void* stream);
 int launch_split_rows(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, void* stream);
 int launch_merge(const MergeArgs& a, int head_dim, void* stream);
+int launch_order(const OrderArgs& a, void* stream);
 int launch_append(const AppendArgs& a, void* stream);
 int launch_scores(const ScoreArgs& a, int64_t units, void* stream);
 

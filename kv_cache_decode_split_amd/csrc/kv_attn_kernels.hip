@@ -209,7 +209,122 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(a.v) + vdst) = vx;
 }
 
+// Exclusive prefix sums of in[0..n) (n <= 256, in[n - 1 - i] when reverse) into out[0..n), by
+// one wave (lane l takes entries 4l .. 4l+3); returns the total. Called by wave 0 alone.
+__device__ unsigned int wave_scan256(const unsigned int* in, unsigned int* out, int n, bool reverse) {
+  const int lane = int(threadIdx.x & 63);
+  unsigned int x[4], sum = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * lane + i;
+    x[i] = idx < n ? in[reverse ? n - 1 - idx : idx] : 0u;
+    sum += x[i];
+  }
+  unsigned int inc = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  unsigned int run = inc - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * lane + i;
+    if (idx < n) out[idx] = run;
+    run += x[i];
+  }
+  return __shfl(inc, 63);
+}
+
+// The (sequence, split) pairs longest first: every whole split (split by split), then each
+// sequence's last partial split by decreasing length (in 256 length classes), then -1 for each
+// empty pair (its workgroups leave after one load). Every non-empty pair appears exactly once
+// whatever the order within a class (positions within a class are taken with LDS atomics).
+// One workgroup.
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const OrderArgs a) {
+  __shared__ unsigned int s_full[kOrderMaxSplits + 1];    // sequences with exactly v whole splits
+  __shared__ unsigned int s_efirst[kOrderMaxSplits + 1];  // sequences whose first empty split is v
+  __shared__ unsigned int s_part[kOrderBuckets];          // partial splits per length class
+  __shared__ unsigned int s_tmp[2][kOrderMaxSplits], s_cnt[2][kOrderMaxSplits];
+  __shared__ unsigned int s_off_full[kOrderMaxSplits], s_off_empty[kOrderMaxSplits];
+  __shared__ unsigned int s_off_part[kOrderBuckets];
+  __shared__ unsigned int s_n_full, s_n_part;
+  const int S = a.num_splits;
+  const int st = a.split_tiles;
+  const int t = int(threadIdx.x);
+  // Visited tiles of a sequence of length ctx, as the split kernel counts them.
+  auto tiles_of = [&](int ctx) {
+    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+    int n_first = 0, win_tile0 = 0;
+    if (a.window > 0) {
+      const int sink_end = min(a.num_sinks, ctx);
+      const int win_start = max(ctx - (a.num_queries - 1) - a.window, 0);
+      n_first = (sink_end + kTile - 1) / kTile;
+      win_tile0 = max(win_start / kTile, n_first);
+    }
+    return n_first + max((ctx + kTile - 1) / kTile - win_tile0, 0);
+  };
+  // This thread's first sequence is loaded before anything else and its tile count kept.
+  const int ctx0 = t < a.batch ? a.ctx_lens[t] : 0;
+  for (int i = t; i <= kOrderMaxSplits; i += kOrderThreads) {
+    s_full[i] = 0u;
+    s_efirst[i] = 0u;
+  }
+  for (int i = t; i < kOrderBuckets; i += kOrderThreads) s_part[i] = 0u;
+  __syncthreads();
+  const int nt0 = tiles_of(ctx0);
+  auto class_of = [&](int len) { return int((int64_t(len) * kOrderBuckets - 1) / st); };  // 1..st-1 -> 0..255
+  for (int b = t; b < a.batch; b += kOrderThreads) {
+    const int nt = b == t ? nt0 : tiles_of(a.ctx_lens[b]);
+    const int nf = min(nt / st, S);
+    const int hp = nf < S && nt > nf * st ? 1 : 0;
+    atomicAdd(&s_full[nf], 1u);
+    if (hp) atomicAdd(&s_part[class_of(nt - nf * st)], 1u);
+    atomicAdd(&s_efirst[nf + hp], 1u);
+  }
+  __syncthreads();
+  // Offsets of the three classes, one wave each (their bases are added where they are used).
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  if (wave == 0) {  // whole splits: split s has B - #{nf <= s} of them
+    wave_scan256(s_full, s_tmp[0], S, false);
+    for (int s = lane; s < S; s += 64) s_cnt[0][s] = unsigned(a.batch) - s_tmp[0][s] - s_full[s];
+    const unsigned int n = wave_scan256(s_cnt[0], s_off_full, S, false);
+    if (lane == 0) s_n_full = n;
+  } else if (wave == 1) {  // partial splits, longest class first
+    const unsigned int n = wave_scan256(s_part, s_off_part, kOrderBuckets, true);
+    if (lane == 0) s_n_part = n;
+  } else if (wave == 2) {  // empty splits: split s is empty for #{first empty split <= s} sequences
+    wave_scan256(s_efirst, s_tmp[1], S, false);
+    for (int s = lane; s < S; s += 64) s_cnt[1][s] = s_tmp[1][s] + s_efirst[s];
+    wave_scan256(s_cnt[1], s_off_empty, S, false);
+  }
+  __syncthreads();
+  const unsigned int base_part = s_n_full;
+  const unsigned int base_empty = s_n_full + s_n_part;
+  for (int b = t; b < a.batch; b += kOrderThreads) {
+    const int nt = b == t ? nt0 : tiles_of(a.ctx_lens[b]);
+    const int nf = min(nt / st, S);
+    const int hp = nf < S && nt > nf * st ? 1 : 0;
+    const int32_t item0 = b * S;
+    for (int s = 0; s < nf; ++s) a.order[atomicAdd(&s_off_full[s], 1u)] = item0 + s;
+    if (hp) {
+      // s_off_part holds the classes in reverse: class c at index kOrderBuckets - 1 - c
+      const int c = class_of(nt - nf * st);
+      a.order[base_part + atomicAdd(&s_off_part[kOrderBuckets - 1 - c], 1u)] = item0 + nf;
+    }
+    for (int s = nf + hp; s < S; ++s) a.order[base_empty + atomicAdd(&s_off_empty[s], 1u)] = -1;  // nothing to do
+  }
+}
+
 }  // namespace
+
+int launch_order(const OrderArgs& a, void* stream) {
+  if (a.num_splits < 1 || a.num_splits > kOrderMaxSplits || a.split_tiles < 1) return int(hipErrorInvalidValue);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a);
+  return int(hipGetLastError());
+}
 
 int launch_split(const SplitArgs& a, const Plan& plan, int head_dim, bool paged, bool q_bf16,
                  bool kv_bf16, void* stream) {

@@ -197,11 +197,26 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
   plan->grid_split = work_units * S;
   const int64_t rows = int64_t(p->batch) * nq * p->num_q_heads;
   plan->grid_merge = S > 1 ? rows : 0;
+  // Unit order: when the split workgroups take several rounds of the device, the ones dispatched
+  // last decide the tail; split by split, those are whatever pairs come last, often long ones.
+  // Longest first leaves the short partial splits for the end (MI355X, C4's ragged batch: split
+  // kernel 1397 -> 1334 us; a list-scheduling model of its measured per-tile times predicted
+  // 1394 -> 1329). KV_ATTN_UNIT_ORDER=0 / =1 overrides the choice where the shape allows it.
+  const char* uo_env = getenv("KV_ATTN_UNIT_ORDER");
+  const int uo_force = uo_env == nullptr ? -1 : strcmp(uo_env, "1") == 0 ? 1 : strcmp(uo_env, "0") == 0 ? 0 : -1;
+  const bool order_ok = S > 1 && S <= kOrderMaxSplits && plan->head_chunks == 1;
+  const bool order_pays = work_units >= int64_t(kOrderMinRounds) * num_cus;
+  plan->unit_order = order_ok && (uo_force >= 0 ? uo_force == 1 : order_pays) ? 1 : 0;
+  plan->order_bytes_offset = 0;
   if (S > 1) {
     const uint64_t o_bytes = uint64_t(rows) * uint64_t(S) * uint64_t(p->head_dim) * 4u;
     const uint64_t o_aligned = (o_bytes + 255u) & ~uint64_t(255u);
     plan->o_part_bytes = o_aligned;
     plan->workspace_bytes = o_aligned + uint64_t(rows) * uint64_t(S) * 2u * 4u;
+    if (plan->unit_order) {
+      plan->order_bytes_offset = (plan->workspace_bytes + 255u) & ~uint64_t(255u);
+      plan->workspace_bytes = plan->order_bytes_offset + uint64_t(p->batch) * uint64_t(S) * 4u;
+    }
   } else {
     plan->o_part_bytes = 0;
     plan->workspace_bytes = 0;

@@ -220,27 +220,41 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   // (0.87 in the same measurement); each wave's state is then a split state of its own.
   const int S = a.num_splits;
   const int units = int(gridDim.x) / S;
-  const int split = blockIdx.x / units;
-  const int unit = blockIdx.x - split * units;
-  // With head chunks (vector path, groups above G heads) consecutive units are the chunks of one
-  // (sequence, KV head): chunk hc serves query heads h0 .. h0 + g - 1 of the group.
   const int hcn = a.head_chunks;
-  const int hc = unit % hcn;
-  const int unit_kv = unit / hcn;
   const bool wave_heads = a.wave_heads != 0;
   const int hpu = wave_heads ? kWaves : 1;      // KV heads per workgroup
   const int units_b = a.h_kv / hpu;             // workgroups per (sequence, split)
-  // The XCD of a workgroup is fixed by its index modulo 8. With fewer than 8 workgroups per
-  // (sequence, split) (wave heads, or h_kv < 8) every split of a sequence would land on the XCDs
-  // of the same residues and a ragged batch would load the XCDs unevenly, so unit u of split s
-  // then serves unit (u + s * units_b) mod (units per split): the sequence index advances by one
-  // per split. MI355X, C4's ragged lengths, split kernel: h_kv = 4 / 2 / 1 0.759 / 0.685 / 0.595
-  // -> 0.779 / 0.723 / 0.612 of peak, C4 with wave heads 0.69 -> 0.74. (With 8 or more per
-  // split every XCD already serves every sequence; there the shift cost C3 0.7 %.)
-  const int units_kv = units / hcn;
-  const int ukv = units_b < 8 ? int((int64_t(unit_kv) + int64_t(split) * units_b) % units_kv) : unit_kv;
-  const int b = ukv / units_b;
-  const int kvh0 = ((ukv - b * units_b + split) % units_b) * hpu;
+  int split, hc, b, kvh0;
+  if (a.order != nullptr) {
+    // Unit order (head_chunks == 1): the (sequence, split) pairs come longest first from the
+    // order list, each served by units_b consecutive workgroups (so by every XCD when units_b is
+    // 8 or more), the empty pairs last as -1; the KV head is rotated by the split index as below.
+    const int item = a.order[blockIdx.x / units_b];
+    if (item < 0) return;  // an empty pair (S > 1: its split state is never read)
+    b = item / S;
+    split = item - b * S;
+    hc = 0;
+    kvh0 = ((int(blockIdx.x % units_b) + split) % units_b) * hpu;
+  } else {
+    split = blockIdx.x / units;
+    const int unit = blockIdx.x - split * units;
+    // With head chunks (vector path, groups above G heads) consecutive units are the chunks of
+    // one (sequence, KV head): chunk hc serves query heads h0 .. h0 + g - 1 of the group.
+    hc = unit % hcn;
+    const int unit_kv = unit / hcn;
+    // The XCD of a workgroup is fixed by its index modulo 8. With fewer than 8 workgroups per
+    // (sequence, split) (wave heads, or h_kv < 8) every split of a sequence would land on the
+    // XCDs of the same residues and a ragged batch would load the XCDs unevenly, so unit u of
+    // split s then serves unit (u + s * units_b) mod (units per split): the sequence index
+    // advances by one per split. MI355X, C4's ragged lengths, split kernel: h_kv = 4 / 2 / 1
+    // 0.759 / 0.685 / 0.595 -> 0.779 / 0.723 / 0.612 of peak, C4 with wave heads 0.69 -> 0.74.
+    // (With 8 or more per split every XCD already serves every sequence; there the shift cost
+    // C3 0.7 %.)
+    const int units_kv = units / hcn;
+    const int ukv = units_b < 8 ? int((int64_t(unit_kv) + int64_t(split) * units_b) % units_kv) : unit_kv;
+    b = ukv / units_b;
+    kvh0 = ((ukv - b * units_b + split) % units_b) * hpu;
+  }
   const int kvh = kvh0 + (wave_heads ? wave : 0);  // this wave's KV head
   const int h0 = hc * G;
   const int g = hcn > 1 ? min(G, a.group - h0) : a.group;  // query heads this workgroup serves

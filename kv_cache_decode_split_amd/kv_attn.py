@@ -124,8 +124,11 @@ class kv_attn_plan(ctypes.Structure):
         ("group_padded", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("wave_heads", ctypes.c_int32),
+        ("unit_order", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
         ("ml_offset", ctypes.c_uint64),
+        ("order_offset", ctypes.c_uint64),
     ]
 
 

@@ -64,7 +64,7 @@ def test_struct_layout_matches_the_header():
 
 
 def test_abi_version_and_status_strings():
-    assert K.kv_attn_abi_version() == 4
+    assert K.kv_attn_abi_version() == 5
     for code in range(9):
         s = K.kv_attn_status_string(code)
         assert s and s != "unknown status"
@@ -172,11 +172,14 @@ def test_plan_covers_every_tile_and_respects_bounds():
             assert L % 16 == 0 and S >= 1
             assert S * L >= T and (S - 1) * L < T          # every position in exactly one split
             assert plan["grid_split"] == B * hkv * S // (4 if wh else 1)
+            uo = 1 < S <= 256 and B * hkv // (4 if wh else 1) >= 4 * cus
+            assert plan["unit_order"] == int(uo), (B, hkv, T, cus)
             if S > 1:
                 # splits of >= 16 tiles when possible (>= 4 per wave either way)
                 assert L // 16 >= min(4 if wh else 16, tiles)
                 assert plan["workspace_bytes"] >= B * hkv * 2 * S * (128 + 2) * 4
                 assert plan["grid_merge"] == B * hkv * 2
+                _check_order_region(plan, B)
             else:
                 assert plan["workspace_bytes"] == 0 and plan["grid_merge"] == 0
             # at most 256 tiles per split with many (sequence, KV head) units, 512 with few
@@ -208,7 +211,52 @@ def test_random_plans_cover_the_visited_tiles_within_the_bounds():
             rows = B * nq * hkv * g
             assert plan["grid_merge"] == rows
             assert plan["workspace_bytes"] >= rows * S * (128 + 2) * 4, label
+            _check_order_region(plan, B)
         assert plan["grid_split"] == B * hkv * S // (4 if wh else 1), label
+        # head_chunks (vector path, groups above 8 heads) keep the split-by-split order
+        halves = plan["group_padded"] == 8 and g > 8
+        uo = 1 < S <= 256 and not halves and B * hkv // (4 if wh else 1) >= 4 * cus
+        assert plan["unit_order"] == int(uo), label
+
+
+def _check_order_region(plan, B):
+    """With unit order the workspace ends with the order list (B * S int32, 256-byte aligned,
+    after the (m, l) array); without it there is none."""
+    S = plan["num_splits"]
+    if plan["unit_order"]:
+        off = plan["order_offset"]
+        assert off % 256 == 0 and off >= plan["ml_offset"]
+        assert plan["workspace_bytes"] == off + B * S * 4
+    else:
+        assert plan["order_offset"] == 0
+
+
+def test_unit_order_rule_and_override(monkeypatch):
+    """C4 on 256 CUs (1024 split workgroups per split) takes the longest-first order; C3 (512),
+    C5 and the unsplit C2 do not; KV_ATTN_UNIT_ORDER forces it either way where the shape allows
+    it (S > 1, S <= 256, no halves)."""
+    def plan(B, hq, hkv, T, cus=256, **kw):
+        return K.kv_attn_get_plan(_params(batch=B, num_q_heads=hq, num_kv_heads=hkv, max_ctx_len=T,
+                                          max_blocks_per_seq=(T + 15) // 16, num_blocks=10**6, **kw), cus)
+    c4 = plan(128, 32, 8, 32768)
+    assert c4["unit_order"] == 1 and c4["num_splits"] == 8
+    assert c4["order_offset"] % 256 == 0 and c4["workspace_bytes"] == c4["order_offset"] + 128 * 8 * 4
+    assert plan(64, 32, 8, 8192)["unit_order"] == 0          # C3: 512 units, two per CU
+    assert plan(4, 64, 8, 131072)["unit_order"] == 0         # C5
+    assert plan(8, 32, 32, 4096)["unit_order"] == 0          # C2: one split
+    assert plan(128, 32, 8, 32768, cus=257)["unit_order"] == 0
+    assert plan(128, 32, 8, 32768, cus=256, num_splits=300)["unit_order"] == 0   # S > 256
+    monkeypatch.setenv("KV_ATTN_UNIT_ORDER", "0")
+    off = plan(128, 32, 8, 32768)
+    assert off["unit_order"] == 0 and off["order_offset"] == 0
+    assert off["workspace_bytes"] <= c4["order_offset"]
+    monkeypatch.setenv("KV_ATTN_UNIT_ORDER", "1")
+    assert plan(64, 32, 8, 8192)["unit_order"] == 1
+    assert plan(2, 8, 8, 700, num_splits=3)["unit_order"] == 1
+    assert plan(2, 8, 8, 700, num_splits=1)["unit_order"] == 0          # one split: nothing to order
+    assert plan(2, 8, 8, 16384, num_splits=600)["unit_order"] == 0      # S = 512 > 256
+    halves = plan(2, 32, 2, 700, num_splits=3, q_dtype=0, kv_dtype=0)   # fp32, group 16: halves
+    assert halves["unit_order"] == 0
 
 
 def test_plan_for_the_five_workloads():
