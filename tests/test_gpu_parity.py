@@ -46,6 +46,12 @@ SMALL = [
     ("C1", dict(batch=3, ctx=(700, 1, 333), head_dim=128, num_q_heads=32, num_kv_heads=4,
                 q_dtype="f32", layout="token_major")),
     ("C3", dict(batch=3, ctx=(1000, 17, 999), capacity=1000, layout="token_major")),
+    # the shapes of two kernel variants that once returned wrong values (both then compiled to
+    # heavily spilling vector kernels): fp32 q with bf16 KV, g = 16, d = 64; fp32 q and KV,
+    # g = 16, d = 128 (also a score-export case)
+    ("C1", dict(batch=3, ctx=(700, 1, 333), head_dim=64, num_q_heads=32, num_kv_heads=2,
+                kv_dtype="bf16")),
+    ("C1", dict(batch=3, ctx=(900, 17, 450), head_dim=128, num_q_heads=32, num_kv_heads=2)),
 ]
 
 
