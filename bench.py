@@ -582,10 +582,14 @@ def measure_decode(args, spec, tag):
         line["config"]["scores"] = ("each layer also writes every attended position's attention "
                                     "weight summed over its KV head's query heads")
     if args.append:
-        line["config"]["append"] = ("each layer appends the current token's K/V before attending"
-                                    if gamma == 1 else
-                                    f"each layer appends the {gamma} draft tokens' K/V before attending")
-        line["append"] = append_info
+        fused = plan["kernel_variant"] in (1, 2)
+        how = ("in the split kernel (the tile holding the new rows takes them from the new-row "
+               "buffers and writes them to the cache)" if fused else "by the append kernel first")
+        line["config"]["append"] = (("each layer appends the current token's K/V, " if gamma == 1 else
+                                     f"each layer appends the {gamma} draft tokens' K/V, ") + how)
+        # The standalone append kernel, for reference (kv_attn_append_decode launches it only on
+        # the fp32 vector path).
+        line["append"] = dict(append_info, kernel="kv_attn_append alone", fused_in_step=fused)
     if traffic is None:
         line["roofline"]["traffic_note"] = traffic_src
     del calls, outs, score_bufs, news

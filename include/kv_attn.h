@@ -296,7 +296,12 @@ kv_attn_status kv_attn_append(const void* k_new, const void* v_new, void* k_cach
  * sequence) and then attended together with the cached ones; with gamma = num_queries > 1 the
  * gamma new tokens are written at ctx_lens[b] - gamma .. ctx_lens[b] - 1 (nothing when
  * ctx_lens[b] < gamma). Arguments as for the two calls; every check of both runs before
- * anything is launched.
+ * anything is launched. With bf16 q and KV (kernel_variant 1 or 2) the append is fused into the
+ * split kernel (Ch. 10 §4: the new K/V is written and used by the same step): the workgroup whose
+ * tile holds a new row takes it from k_new / v_new and writes it into the cache, and no append
+ * kernel is launched; the caches end up byte-identical to the two separate calls, and the output
+ * equal up to rounding (that split visits its tiles in order). The fp32 vector path launches the
+ * append kernel first.
  */
 kv_attn_status kv_attn_append_decode(const void* q, const void* k_new, const void* v_new,
                                      void* k_cache, void* v_cache, const int32_t* block_table,

@@ -246,7 +246,12 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
                        ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.o_part_bytes)
                        : nullptr;
 
-  if (passes & kPassAppend) {
+  // The append fuses into the split kernel in the bf16 matrix-core variants (the tile holding
+  // the new rows takes them from k_new / v_new and writes them into the cache); otherwise the
+  // append kernel writes them first.
+  const bool fused_append = (passes & kPassAppend) && (passes & kPassSplit) && !scores &&
+                            (plan.variant == 2 || (plan.variant == 1 && plan.group_padded <= kAppendMaxGroup));
+  if ((passes & kPassAppend) && !fused_append) {
     // The current token(s) are the last positions ctx_lens[b] counts: write them before reading.
     const int32_t nq = p->num_queries > 1 ? p->num_queries : 1;
     const AppendArgs ap = append_args(p, k_new, v_new, const_cast<void*>(k_cache),
@@ -287,6 +292,8 @@ kv_attn_status decode_impl(int passes, const void* q, const void* k_cache, const
     a.row_stats = plan.num_splits == 1 ? row_stats : nullptr;
     const double scale = p->scale != 0.0f ? double(p->scale) : 1.0 / sqrt(double(p->head_dim));
     a.scale_log2 = float(scale * 1.4426950408889634);  // log2(e)
+    a.k_new = fused_append ? k_new : nullptr;
+    a.v_new = fused_append ? v_new : nullptr;
     a.order = nullptr;
     if (plan.unit_order && !scores) {  // the score export keeps the split-by-split order
       int32_t* order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.order_bytes_offset);

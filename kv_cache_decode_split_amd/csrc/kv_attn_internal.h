@@ -26,6 +26,7 @@ constexpr int kMaxQueries = 16;
 constexpr int kRowsMinGroup = 4;      // one query token: rows mode from this group size on (bf16)
 constexpr int kVectorMaxGroup = 8;    // vector path: query heads one workgroup holds
 constexpr int kWaveHeadsMinTiles = 32; // wave heads: tiles per wave, at least, on a full device
+constexpr int kAppendMaxGroup = 4;     // fused append: padded groups of variant 1 it serves
 constexpr int kOrderMaxSplits = 256;   // unit order: splits per sequence, at most (one lane
                                        // of a wave scans 4 counters each)
 constexpr int kOrderThreads = 256;    // unit order: the order kernel's one workgroup
@@ -66,6 +67,8 @@ struct SplitArgs {
                                // position (one query token per sequence only)
   int64_t logits_ld;           // multiple of kTile, >= max_ctx rounded up to kTile
   float* row_stats;            // nullptr, or [B * h_q, 2]: final (m, l) per row (num_splits == 1)
+  const void* k_new;           // nullptr, or the fused append's new K rows [B, nq, h_kv, d]
+  const void* v_new;           // (bf16, matrix-core variants); k and v are then writable
   const int32_t* order;        // nullptr, or [B * S]: entry i = b * S + split of the i-th
                                // (sequence, split) pair to serve, or -1 for an empty pair
                                // (head_chunks == 1); its workgroups are the next

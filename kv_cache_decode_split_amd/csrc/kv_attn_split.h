@@ -157,6 +157,18 @@ __device__ __forceinline__ Seg<BYTES> load_seg(const char* p) {
   return s;
 }
 
+template <int BYTES>
+__device__ __forceinline__ void store_seg(char* p, const Seg<BYTES>& s) {
+  if constexpr (BYTES == 8) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{s.w[0], s.w[1]};
+  } else {
+    static_for<0, BYTES / 16>([&](auto I) __attribute__((always_inline)) {
+      *reinterpret_cast<u32x4_t*>(p + 16 * I()) =
+          u32x4_t{s.w[4 * I() + 0], s.w[4 * I() + 1], s.w[4 * I() + 2], s.w[4 * I() + 3]};
+    });
+  }
+}
+
 // Exact widening of N stored elements to fp32 (bf16: the 16 bits become the high half).
 template <int N, bool BF16, int BYTES>
 __device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
@@ -183,10 +195,11 @@ __device__ __forceinline__ void widen(const Seg<BYTES>& s, float (&f)[N]) {
 // a.logits and, with one split, each row's final (m, l) to a.row_stats. A separate
 // instantiation, so that the kernels without it keep their register allocation.
 template <int D, int G, bool Q_BF16, bool KV_BF16, bool MFMA, int PAGED, int R = 0,
-          bool SCORES = false>
+          bool SCORES = false, bool APPEND = false>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(!MFMA || (Q_BF16 && KV_BF16), "matrix-core scores need bf16 q and KV");
+  static_assert(!APPEND || (MFMA && !SCORES), "the fused append serves the matrix-core variants");
   static_assert(R == 0 || MFMA, "rows mode runs on the matrix cores");
   static_assert(!(SCORES && R > 1), "score export takes one query token per sequence");
   constexpr bool ROWS = R > 0;
@@ -263,6 +276,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int nq = ROWS ? a.num_queries : 1;  // query tokens per sequence (the last nq positions)
+  // Fused append: the nq new tokens' K/V rows sit at positions new0 .. ctx - 1 (none when
+  // ctx < nq). The tile that holds them takes those rows from k_new / v_new instead of the cache
+  // and writes them into the cache (no other workgroup reads them in this launch).
+  const int new0 = (APPEND && ctx >= nq) ? ctx - nq : -1;
   // Attended positions: all of [0, ctx), or with a window W the sinks [0, sink_end) and the
   // recent positions [win_start, ctx) (with nq query tokens, the union of their windows). Their
   // tiles are enumerated as "visited" tiles: the n_first tiles of the sink range, then the tiles
@@ -314,7 +331,11 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   // order and contiguous caches unchanged. The visiting order inside a split only changes the
   // rounding of the running state.
   const int span = t_end - t_begin;
-  const int rot = span > 0 ? int((int64_t(split) * 61) % span) : 0;
+  // Fused append: the split whose last visited tile holds new rows keeps its tiles in order, so
+  // the tiles with new rows are the last ones each wave visits.
+  const int last_tile = t_end - 1 < n_first ? t_end - 1 : win_tile0 + (t_end - 1 - n_first);
+  const bool split_has_new = APPEND && new0 >= 0 && span > 0 && (last_tile + 1) * kTile > new0;
+  const int rot = span > 0 && !split_has_new ? int((int64_t(split) * 61) % span) : 0;
   auto visit = [&](int k) __attribute__((always_inline)) {
     int j = woff + wstride * k + rot;
     if (j >= span) j -= span;
@@ -444,9 +465,17 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
     u32x4_t kc[KC];      // variant 1: key row r16, 32-element chunks
     Seg<SEG> kr[4];      // variant 0: key rows 4*q4+i
     Seg<SEG> vr[4];      // value rows 4*q4+i
+    const char* kt;      // fused append: the tile's K and V rows in the cache (row 0)
+    const char* vt;
+  };
+  // Fused append: element offset of new row j (position new0 + j) of this KV head in k_new /
+  // v_new ([B, nq, h_kv, D]).
+  auto new_row = [&](int j) __attribute__((always_inline)) {
+    return ((int64_t(b) * nq + j) * a.h_kv + kvh) * D;
   };
 
-  auto load_tile = [&](int k, Frag& f) __attribute__((always_inline)) {
+  // patch (fused append only, set for a wave's last tiles): the tile may hold new rows.
+  auto load_tile = [&](int k, Frag& f, auto patch) __attribute__((always_inline)) {
     const int tile = logical_tile(visit(k));
     const int p0 = tile * kTile;
     int64_t koff, voff;             // element offset of tile row 0
@@ -478,6 +507,45 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.vr[i] = load_seg<SEG>(vt + o.v[i]);
+    if constexpr (APPEND && decltype(patch)::value) {
+      f.kt = kt;
+      f.vt = vt;
+      if (new0 >= 0 && p0 + kTile > new0) {
+        // Every row a lane loaded from a new position (its own row, or the attended row an
+        // unattended one was redirected to) comes from k_new / v_new: the cache does not hold it
+        // yet, and a value row must be finite even where its probability is 0.
+        auto loaded = [&](int m) __attribute__((always_inline)) {
+          return whole || attended_at(p0, m) ? m : anchor;
+        };
+        const char* kn = reinterpret_cast<const char*>(a.k_new);
+        const char* vn = reinterpret_cast<const char*>(a.v_new);
+        const int mk = loaded(r16);
+        if (p0 + mk >= new0) {
+#pragma unroll
+          for (int c = 0; c < KC; ++c)
+            f.kc[c] = *reinterpret_cast<const u32x4_t*>(kn + (new_row(p0 + mk - new0) + c * 32 + q4 * 8) * 2);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mv = loaded(4 * q4 + i);
+          if (p0 + mv >= new0) f.vr[i] = load_seg<SEG>(vn + (new_row(p0 + mv - new0) + r16 * EPL) * 2);
+        }
+      }
+    }
+  };
+  // Fused append: the lanes holding an attended new row write it into the cache once its data
+  // has arrived (at compute time, so that no earlier load in flight is waited for).
+  auto store_new_rows = [&](const Frag& f, int p0) __attribute__((always_inline)) {
+    if (new0 < 0 || p0 + kTile <= new0) return;
+    char* kw = const_cast<char*>(f.kt);  // the caller's writable caches in append mode
+    char* vw = const_cast<char*>(f.vt);
+    if (p0 + r16 >= new0 && attended_at(p0, r16)) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) *reinterpret_cast<u32x4_t*>(kw + full.k + c * 64) = f.kc[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p0 + 4 * q4 + i >= new0 && attended_at(p0, 4 * q4 + i)) store_seg<SEG>(vw + full.v[i], f.vr[i]);
   };
 
   // Score export: the scores of positions pos .. pos+3 for query head j of this (sequence, KV
@@ -675,51 +743,83 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
         oT[cb][dc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[dc], p_b, oT[cb][dc], 0, 0, 0);
     }
   };
-  auto compute = [&](int k, const Frag& f) __attribute__((always_inline)) {
+  auto compute = [&](int k, const Frag& f, auto patch) __attribute__((always_inline)) {
+    if constexpr (APPEND && decltype(patch)::value) store_new_rows(f, logical_tile(visit(k)) * kTile);
     if constexpr (ROWS)
       compute_rows(k, f);
     else
       compute_tile(k, f);
   };
+  constexpr std::false_type kPlain{};
+  constexpr std::bool_constant<APPEND> kPatch{};
 
   // ---- streaming loop: DEPTH tiles in flight --------------------------------------------------
   // The steady-state loop issues its loads unconditionally, so the compiler's wait counts let
   // the DEPTH tiles behind the one being computed stay in flight; the last tiles are drained
-  // with conditional loads outside it.
+  // with conditional loads outside it. With the fused append a wave's last kTail tiles (where
+  // the new rows can be: the split that holds them is not rotated) stay out of the steady loop,
+  // so that its code and wait counts are those of the plain kernel.
+  constexpr int kTail = APPEND ? 2 : 0;
   Frag buf[DEPTH];
   if (paged && n_w > 0) fetch_block_ids(0);
   int k0 = 0;
-  if (n_w >= 2 * DEPTH) {
-    static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) { load_tile(P(), buf[P()]); });
+  if (n_w >= 2 * DEPTH + kTail) {
+    static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) { load_tile(P(), buf[P()], kPlain); });
     do {
       static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
-        compute(k0 + P(), buf[P()]);
-        load_tile(k0 + P() + DEPTH, buf[P()]);
+        compute(k0 + P(), buf[P()], kPlain);
+        load_tile(k0 + P() + DEPTH, buf[P()], kPlain);
       });
       k0 += DEPTH;
-    } while (k0 + 2 * DEPTH <= n_w);
-    // Tiles k0 .. k0+DEPTH-1 are in flight; at most DEPTH-1 more remain after them.
+    } while (k0 + 2 * DEPTH + kTail <= n_w);
+    if constexpr (APPEND) {
+      // Tiles k0 .. k0+DEPTH-1 are in flight; at most DEPTH-1+kTail more remain after them.
+      for (; k0 < n_w; k0 += DEPTH) {
+        static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
+          const int k = k0 + P();
+          if (k < n_w) {
+            compute(k, buf[P()], kPatch);
+            if (k + DEPTH < n_w) load_tile(k + DEPTH, buf[P()], kPatch);
+          }
+        });
+      }
+    } else {
+      // Tiles k0 .. k0+DEPTH-1 are in flight; at most DEPTH-1 more remain after them.
+      static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
+        const int k = k0 + P();
+        compute(k, buf[P()], kPlain);
+        if (k + DEPTH < n_w) load_tile(k + DEPTH, buf[P()], kPlain);
+      });
+      static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
+        const int k = k0 + DEPTH + P();
+        if (k < n_w) compute(k, buf[P()], kPlain);
+      });
+    }
+  } else if constexpr (APPEND) {
     static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
-      const int k = k0 + P();
-      compute(k, buf[P()]);
-      if (k + DEPTH < n_w) load_tile(k + DEPTH, buf[P()]);
+      if (P() < n_w) load_tile(P(), buf[P()], kPatch);
     });
-    static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
-      const int k = k0 + DEPTH + P();
-      if (k < n_w) compute(k, buf[P()]);
-    });
+    for (; k0 < n_w; k0 += DEPTH) {
+      static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
+        const int k = k0 + P();
+        if (k < n_w) {
+          compute(k, buf[P()], kPatch);
+          if (k + DEPTH < n_w) load_tile(k + DEPTH, buf[P()], kPatch);
+        }
+      });
+    }
   } else {
     static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
-      if (P() < n_w) load_tile(P(), buf[P()]);
+      if (P() < n_w) load_tile(P(), buf[P()], kPlain);
     });
     static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
       if (P() < n_w) {
-        compute(P(), buf[P()]);
-        if (P() + DEPTH < n_w) load_tile(P() + DEPTH, buf[P()]);
+        compute(P(), buf[P()], kPlain);
+        if (P() + DEPTH < n_w) load_tile(P() + DEPTH, buf[P()], kPlain);
       }
     });
     static_for<0, DEPTH>([&](auto P) __attribute__((always_inline)) {
-      if (DEPTH + P() < n_w) compute(DEPTH + P(), buf[P()]);
+      if (DEPTH + P() < n_w) compute(DEPTH + P(), buf[P()], kPlain);
     });
   }
 
@@ -834,20 +934,27 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   }
 }
 
-template <int D, int G, bool QB, bool KB, bool MF, int PG, int R = 0, bool SC = false>
+template <int D, int G, bool QB, bool KB, bool MF, int PG, int R = 0, bool SC = false, bool AP = false>
 int launch_one(const SplitArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG, R, SC>), dim3(uint32_t(grid)),
+  hipLaunchKernelGGL((split_kernel<D, G, QB, KB, MF, PG, R, SC, AP>), dim3(uint32_t(grid)),
                      dim3(kSplitThreads), 0, stream, a);
   return int(hipGetLastError());
 }
 
 // Variant 1 (bf16 q and KV, matrix-core scores, VALU P.V), cache layout compiled in; with
-// a.logits set, the score-export instantiation.
+// a.logits set, the score-export instantiation; with a.k_new set, the fused append.
 template <int D, int G>
 int launch_mfma_group(const SplitArgs& a, const Plan& plan, bool paged, hipStream_t s) {
   if (a.logits != nullptr)
     return paged ? launch_one<D, G, true, true, true, 1, 0, true>(a, plan.grid_split, s)
                  : launch_one<D, G, true, true, true, 0, 0, true>(a, plan.grid_split, s);
+  if (a.k_new != nullptr) {
+    // Variant 1 serves groups of at most 3 heads (rows mode takes 4 or more), so G <= 4.
+    if constexpr (G <= kAppendMaxGroup)
+      return paged ? launch_one<D, G, true, true, true, 1, 0, false, true>(a, plan.grid_split, s)
+                   : launch_one<D, G, true, true, true, 0, 0, false, true>(a, plan.grid_split, s);
+    return int(hipErrorInvalidValue);
+  }
   return paged ? launch_one<D, G, true, true, true, 1>(a, plan.grid_split, s)
                : launch_one<D, G, true, true, true, 0>(a, plan.grid_split, s);
 }
@@ -899,6 +1006,15 @@ int launch_rows(const SplitArgs& a, const Plan& plan, bool paged, hipStream_t s)
     if (plan.row_blocks != 1 || plan.num_queries != 1) return int(hipErrorInvalidValue);
     return paged ? launch_one<D, 1, true, true, true, 1, 1, true>(a, plan.grid_split, s)
                  : launch_one<D, 1, true, true, true, 0, 1, true>(a, plan.grid_split, s);
+  }
+  if (a.k_new != nullptr) {  // the fused append
+    switch (plan.row_blocks) {
+      case 1: return paged ? launch_one<D, 1, true, true, true, 1, 1, false, true>(a, plan.grid_split, s)
+                           : launch_one<D, 1, true, true, true, 0, 1, false, true>(a, plan.grid_split, s);
+      case 2: return paged ? launch_one<D, 1, true, true, true, 1, 2, false, true>(a, plan.grid_split, s)
+                           : launch_one<D, 1, true, true, true, 0, 2, false, true>(a, plan.grid_split, s);
+      default: return int(hipErrorInvalidValue);
+    }
   }
   switch (plan.row_blocks) {
     case 1: return paged ? launch_one<D, 1, true, true, true, 1, 1>(a, plan.grid_split, s)
