@@ -170,8 +170,9 @@ typedef struct kv_attn_plan {
   int32_t reserved;         /* 0 */
   uint64_t workspace_bytes; /* workspace kv_attn_decode needs (0 when S == 1) */
   uint64_t ml_offset;       /* byte offset of the (m, l) array inside the workspace (S > 1) */
-  uint64_t order_offset;    /* byte offset of the order list (batch * S int32) inside the
-                               workspace when unit_order, else 0 */
+  uint64_t order_offset;    /* byte offset of the order list (batch * S pairs of int32: the
+                               pair's index b * S + split, or -1, and the sequence's clamped
+                               length) inside the workspace when unit_order, else 0 */
 } kv_attn_plan;
 
 /* ABI version of the loaded library (KV_ATTN_ABI_VERSION it was built with). */

@@ -69,16 +69,16 @@ struct SplitArgs {
   float* row_stats;            // nullptr, or [B * h_q, 2]: final (m, l) per row (num_splits == 1)
   const void* k_new;           // nullptr, or the fused append's new K rows [B, nq, h_kv, d]
   const void* v_new;           // (bf16, matrix-core variants); k and v are then writable
-  const int32_t* order;        // nullptr, or [B * S]: entry i = b * S + split of the i-th
-                               // (sequence, split) pair to serve, or -1 for an empty pair
-                               // (head_chunks == 1); its workgroups are the next
-                               // units-per-split indices
+  const int32_t* order;        // nullptr, or [B * S][2]: entry i = (b * S + split, clamped
+                               // length of b) of the i-th (sequence, split) pair to serve, or
+                               // (-1, 0) for an empty pair (head_chunks == 1); its workgroups
+                               // are the next units-per-split indices
 };
 
 // The order kernel: a permutation of the B * S (sequence, split) pairs, longest first.
 struct OrderArgs {
   const int32_t* ctx_lens;
-  int32_t* order;              // [B * S]: the non-empty pairs longest first, then -1 each
+  int32_t* order;              // [B * S][2]: the non-empty pairs longest first, then (-1, 0) each
   int32_t batch;
   int32_t num_splits;          // S <= kOrderMaxSplits
   int32_t split_tiles;
@@ -160,7 +160,7 @@ struct Plan {
   int64_t grid_merge;
   uint64_t workspace_bytes;
   uint64_t o_part_bytes;  // offset of ml_part inside the workspace
-  uint64_t order_bytes_offset;  // offset of the order list (batch * S int32) when unit_order
+  uint64_t order_bytes_offset;  // offset of the order list (batch * S int32 pairs) when unit_order
 };
 
 // Host-only helpers (kv_attn_plan.cpp; no HIP calls).

@@ -236,9 +236,10 @@ __device__ unsigned int wave_scan256(const unsigned int* in, unsigned int* out, 
   return __shfl(inc, 63);
 }
 
-// The (sequence, split) pairs longest first: every whole split (split by split), then each
-// sequence's last partial split by decreasing length (in 256 length classes), then -1 for each
-// empty pair (its workgroups leave after one load). Every non-empty pair appears exactly once
+// The (sequence, split) pairs longest first, each listed with its sequence's clamped length:
+// every whole split (split by split), then each sequence's last partial split by decreasing
+// length (in 256 length classes), then -1 for each empty pair (its workgroups leave after one
+// load). Every non-empty pair appears exactly once
 // whatever the order within a class (positions within a class are taken with LDS atomics).
 // One workgroup.
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const OrderArgs a) {
@@ -252,9 +253,10 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const OrderArgs a)
   const int S = a.num_splits;
   const int st = a.split_tiles;
   const int t = int(threadIdx.x);
+  auto clamp_len = [&](int ctx) { return ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx); };
   // Visited tiles of a sequence of length ctx, as the split kernel counts them.
   auto tiles_of = [&](int ctx) {
-    ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+    ctx = clamp_len(ctx);
     int n_first = 0, win_tile0 = 0;
     if (a.window > 0) {
       const int sink_end = min(a.num_sinks, ctx);
@@ -302,18 +304,20 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const OrderArgs a)
   __syncthreads();
   const unsigned int base_part = s_n_full;
   const unsigned int base_empty = s_n_full + s_n_part;
+  int2* list = reinterpret_cast<int2*>(a.order);
   for (int b = t; b < a.batch; b += kOrderThreads) {
-    const int nt = b == t ? nt0 : tiles_of(a.ctx_lens[b]);
+    const int len = clamp_len(b == t ? ctx0 : a.ctx_lens[b]);
+    const int nt = b == t ? nt0 : tiles_of(len);
     const int nf = min(nt / st, S);
     const int hp = nf < S && nt > nf * st ? 1 : 0;
     const int32_t item0 = b * S;
-    for (int s = 0; s < nf; ++s) a.order[atomicAdd(&s_off_full[s], 1u)] = item0 + s;
+    for (int s = 0; s < nf; ++s) list[atomicAdd(&s_off_full[s], 1u)] = int2{item0 + s, len};
     if (hp) {
       // s_off_part holds the classes in reverse: class c at index kOrderBuckets - 1 - c
       const int c = class_of(nt - nf * st);
-      a.order[base_part + atomicAdd(&s_off_part[kOrderBuckets - 1 - c], 1u)] = item0 + nf;
+      list[base_part + atomicAdd(&s_off_part[kOrderBuckets - 1 - c], 1u)] = int2{item0 + nf, len};
     }
-    for (int s = nf + hp; s < S; ++s) a.order[base_empty + atomicAdd(&s_off_empty[s], 1u)] = -1;  // nothing to do
+    for (int s = nf + hp; s < S; ++s) list[base_empty + atomicAdd(&s_off_empty[s], 1u)] = int2{-1, 0};  // nothing to do
   }
 }
 

@@ -215,7 +215,7 @@ kv_attn_status make_plan(const kv_attn_params* p, int32_t num_cus, Plan* plan) {
     plan->workspace_bytes = o_aligned + uint64_t(rows) * uint64_t(S) * 2u * 4u;
     if (plan->unit_order) {
       plan->order_bytes_offset = (plan->workspace_bytes + 255u) & ~uint64_t(255u);
-      plan->workspace_bytes = plan->order_bytes_offset + uint64_t(p->batch) * uint64_t(S) * 4u;
+      plan->workspace_bytes = plan->order_bytes_offset + uint64_t(p->batch) * uint64_t(S) * 8u;
     }
   } else {
     plan->o_part_bytes = 0;

@@ -238,12 +238,15 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   const int hpu = wave_heads ? kWaves : 1;      // KV heads per workgroup
   const int units_b = a.h_kv / hpu;             // workgroups per (sequence, split)
   int split, hc, b, kvh0;
+  int ctx_listed = 0;  // unit order: the pair's clamped length, listed with it
   if (a.order != nullptr) {
     // Unit order (head_chunks == 1): the (sequence, split) pairs come longest first from the
     // order list, each served by units_b consecutive workgroups (so by every XCD when units_b is
     // 8 or more), the empty pairs last as -1; the KV head is rotated by the split index as below.
-    const int item = a.order[blockIdx.x / units_b];
+    const int2 entry = reinterpret_cast<const int2*>(a.order)[blockIdx.x / units_b];
+    const int item = entry.x;
     if (item < 0) return;  // an empty pair (S > 1: its split state is never read)
+    ctx_listed = entry.y;
     b = item / S;
     split = item - b * S;
     hc = 0;
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(const SplitArgs a)
   const int g = hcn > 1 ? min(G, a.group - h0) : a.group;  // query heads this workgroup serves
   const bool paged = PAGED == 2 ? (a.block_table != nullptr) : (PAGED == 1);
 
-  int ctx = a.ctx_lens[b];
+  int ctx = a.order != nullptr ? ctx_listed : a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   const int nq = ROWS ? a.num_queries : 1;  // query tokens per sequence (the last nq positions)
   // Fused append: the nq new tokens' K/V rows sit at positions new0 .. ctx - 1 (none when

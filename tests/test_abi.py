@@ -220,13 +220,13 @@ def test_random_plans_cover_the_visited_tiles_within_the_bounds():
 
 
 def _check_order_region(plan, B):
-    """With unit order the workspace ends with the order list (B * S int32, 256-byte aligned,
+    """With unit order the workspace ends with the order list (B * S int32 pairs, 256-byte aligned,
     after the (m, l) array); without it there is none."""
     S = plan["num_splits"]
     if plan["unit_order"]:
         off = plan["order_offset"]
         assert off % 256 == 0 and off >= plan["ml_offset"]
-        assert plan["workspace_bytes"] == off + B * S * 4
+        assert plan["workspace_bytes"] == off + B * S * 8
     else:
         assert plan["order_offset"] == 0
 
@@ -240,7 +240,7 @@ def test_unit_order_rule_and_override(monkeypatch):
                                           max_blocks_per_seq=(T + 15) // 16, num_blocks=10**6, **kw), cus)
     c4 = plan(128, 32, 8, 32768)
     assert c4["unit_order"] == 1 and c4["num_splits"] == 8
-    assert c4["order_offset"] % 256 == 0 and c4["workspace_bytes"] == c4["order_offset"] + 128 * 8 * 4
+    assert c4["order_offset"] % 256 == 0 and c4["workspace_bytes"] == c4["order_offset"] + 128 * 8 * 8
     assert plan(64, 32, 8, 8192)["unit_order"] == 0          # C3: 512 units, two per CU
     assert plan(4, 64, 8, 131072)["unit_order"] == 0         # C5
     assert plan(8, 32, 32, 4096)["unit_order"] == 0          # C2: one split

@@ -94,8 +94,9 @@ def test_order_list_is_a_longest_first_permutation(over, monkeypatch):
     _, call = _decode(w, monkeypatch, True, 6)
     plan = call.plan()
     B, S, st = spec.batch, plan["num_splits"], plan["split_len"] // 16
-    raw = call.workspace[plan["order_offset"]:plan["order_offset"] + 4 * B * S]
-    order = raw.cpu().numpy().view(np.int32)
+    raw = call.workspace[plan["order_offset"]:plan["order_offset"] + 8 * B * S]
+    pairs = raw.cpu().numpy().view(np.int32).reshape(B * S, 2)
+    order, listed = pairs[:, 0], pairs[:, 1]
     ctx = w.ctx_lens.cpu().numpy()
     size = {}
     for b in range(B):
@@ -107,6 +108,8 @@ def test_order_list_is_a_longest_first_permutation(over, monkeypatch):
     n_busy = len(busy)
     assert sorted(order[:n_busy].tolist()) == busy
     assert (order[n_busy:] == -1).all() and len(order) - n_busy == B * S - len(busy)
+    # each pair carries its sequence's clamped length
+    assert all(int(listed[i]) == min(max(int(ctx[int(order[i]) // S]), 0), w.max_ctx_len) for i in range(n_busy))
     sizes = [size[int(item)] for item in order[:n_busy]]
     # class of a pair: 0 whole, 1 + (255 - length class) partial
     cls = [0 if n == st else 1 + 255 - (n * 256 - 1) // st for n in sizes]
