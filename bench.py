@@ -533,7 +533,7 @@ def measure_decode(args, spec, tag):
             "block_order": spec.block_order if spec.paged else None,
             "unique_kv_bytes_per_step": kv_bytes_step, "flops_per_step": flops_step,
             "plan": {k: plan[k] for k in ("num_splits", "split_len", "grid_split", "grid_merge",
-                                          "kernel_variant", "wave_heads", "num_cus")},
+                                          "kernel_variant", "wave_heads", "unit_order", "num_cus")},
             "parallelism": "single GPU",
         },
         "roofline": {
