@@ -187,8 +187,9 @@ def kv_attn_status_string(status: int) -> str:
 def kv_attn_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
     """Stream every byte of ``src`` (a contiguous CUDA tensor) once with the read probe, on the
     current stream; ``sink`` is a CUDA tensor with at least one 32-bit element."""
-    if not (src.is_cuda and sink.is_cuda and src.is_contiguous()):
-        raise ValueError("read probe: src and sink must be CUDA tensors, src contiguous")
+    if not (src.is_cuda and sink.is_cuda and src.is_contiguous()) or sink.device != src.device:
+        raise ValueError("read probe: src and sink must be CUDA tensors on one device, src contiguous")
+    _check_device(src, "src")
     if sink.numel() < 1 or sink.element_size() != 4:
         raise ValueError("read probe: sink must hold a 32-bit word")
     stream = torch.cuda.current_stream(src.device).cuda_stream
@@ -266,6 +267,17 @@ def _hold_for_stream(t: Optional[torch.Tensor], stream) -> None:
         t.record_stream(stream)
 
 
+def _check_device(t: torch.Tensor, what: str) -> None:
+    """The library takes device pointers and launches on the current device: a host tensor, or
+    one on another device, is refused here rather than handed to a kernel."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device (CUDA) tensor, not on {t.device}")
+    current = torch.cuda.current_device()
+    if t.device.index != current:
+        raise ValueError(f"{what} is on {t.device} but the library launches on the current device "
+                         f"cuda:{current}")
+
+
 def _check_extent(t: torch.Tensor, strides, blocks: int, slots: int, heads: int, d: int, what: str):
     last = (blocks - 1) * strides[0] + (slots - 1) * strides[1] + (heads - 1) * strides[2] + d - 1
     avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
@@ -303,6 +315,7 @@ class DecodeCall:
         if k_cache.dtype != v_cache.dtype:
             raise ValueError("k_cache and v_cache must share a dtype")
         dev = q.device
+        _check_device(q, "q")
         for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens),
                         ("out", out)):
             if t.device != dev:
@@ -467,6 +480,9 @@ def kv_attn_append(k_new, v_new, k_cache, v_cache, block_table, positions, *, nu
     B = int(positions.shape[0])
     d = int(k_new.shape[-1])
     n = int(k_new.shape[1]) if k_new.dim() == 4 else 1
+    _check_device(k_cache, "k_cache")
+    if v_cache.device != k_cache.device or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must share k_cache's device and dtype")
     _check_new_rows(k_new, v_new, k_cache, B, num_kv_heads, d, n)
     if positions.dtype != torch.int32 or not positions.is_contiguous() or positions.device != k_cache.device:
         raise ValueError("positions must be a contiguous int32 [B] tensor on the cache's device")
@@ -530,14 +546,16 @@ def kv_attn_merge(o_partial: torch.Tensor, ml_partial: torch.Tensor,
     if o_partial.dim() != 3 or ml_partial.dim() != 3:
         raise ValueError("o_partial must be [rows, S, d] and ml_partial [rows, S, 2]")
     rows, S, d = o_partial.shape
+    _check_device(o_partial, "o_partial")
     if ml_partial.shape != (rows, S, 2) or out.shape != (rows, d):
         raise ValueError("shape mismatch between o_partial, ml_partial and out")
     for t in (o_partial, ml_partial, out):
         if t.dtype != torch.float32 or not t.is_contiguous() or t.device != o_partial.device:
             raise ValueError("merge tensors must be contiguous fp32 on one device")
     if num_valid is not None and (num_valid.dtype != torch.int32 or num_valid.shape != (rows,)
-                                  or not num_valid.is_contiguous()):
-        raise ValueError("num_valid must be a contiguous int32 [rows] tensor")
+                                  or not num_valid.is_contiguous()
+                                  or num_valid.device != o_partial.device):
+        raise ValueError("num_valid must be a contiguous int32 [rows] tensor on the same device")
     st = _lib.kv_attn_merge(o_partial.data_ptr(), ml_partial.data_ptr(),
                             None if num_valid is None else num_valid.data_ptr(), out.data_ptr(),
                             rows, S, d, _stream_handle(stream))

@@ -12,7 +12,7 @@ from typing import Optional
 
 import torch
 
-from .kv_attn import _hold_for_stream, _lib, _stream_handle, KvAttnError, KV_ATTN_OK
+from .kv_attn import _check_device, _hold_for_stream, _lib, _stream_handle, KvAttnError, KV_ATTN_OK
 
 __all__ = ["kv_evict_params", "make_evict_params", "kv_evict_workspace_size", "kv_evict_select",
            "EXPORTED_SYMBOLS"]
@@ -65,6 +65,7 @@ def kv_evict_select(scores: torch.Tensor, budget: int, current: Optional[int] = 
     """
     if scores.dim() != 3 or scores.dtype != torch.float32 or not scores.is_cuda:
         raise ValueError("scores must be an fp32 [L, H, N] tensor on a GPU")
+    _check_device(scores, "scores")
     L, H, N = scores.shape
     if scores.stride(2) != 1 or (H > 1 and L > 1 and scores.stride(0) != H * scores.stride(1)):
         raise ValueError("scores rows must be equally spaced with a contiguous last axis")
@@ -89,6 +90,8 @@ def kv_evict_select(scores: torch.Tensor, budget: int, current: Optional[int] = 
     own_workspace = bool(need) and workspace is None
     if own_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    elif workspace is not None and workspace.device != scores.device:
+        raise ValueError("workspace must be on the scores' device")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.kv_evict_select(scores.data_ptr(), keep.data_ptr(),

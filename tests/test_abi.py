@@ -423,13 +423,37 @@ def test_host_validator():
 
 
 def test_binding_rejects_tensors_too_small_for_the_strides():
+    k = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)  # contiguous head major, capacity 8
+    strides = (2 * 8 * 64, 64, 8 * 64)
+    K._check_extent(k, strides, 2, 8, 2, 64, "k_cache")  # exactly the tensor: accepted
+    with pytest.raises(ValueError, match="strides address"):
+        K._check_extent(k, strides, 2, 9, 2, 64, "k_cache")  # a ninth slot per block
+    with pytest.raises(ValueError, match="strides address"):
+        K._check_extent(k[1:], strides, 2, 8, 2, 64, "k_cache")  # a view that starts later
+
+
+def test_binding_refuses_host_tensors_before_any_library_call():
+    """Host tensors would reach the kernels as host addresses: every entry of the binding that
+    takes tensors refuses them first."""
+    from kv_cache_decode_split_amd import kv_evict as E
     q = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
     out = torch.zeros(2, 4, 64, dtype=torch.float32)
-    k = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)  # contiguous head major, capacity 8
+    k = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)
     ctx = torch.tensor([8, 8], dtype=torch.int32)
+    strides = (2 * 8 * 64, 64, 8 * 64)
+    with pytest.raises(ValueError, match="device"):
+        K.kv_attn_decode(q, k, k, None, ctx, out, num_kv_heads=2, k_strides=strides,
+                         v_strides=strides, block_size=8, num_blocks=2, max_ctx_len=8)
+    rows = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        K.kv_attn_append(rows, rows, k, k, None, torch.zeros(2, dtype=torch.int32), num_kv_heads=2,
+                         k_strides=strides, v_strides=strides, block_size=8, num_blocks=2)
+    with pytest.raises(ValueError, match="device"):
+        K.kv_attn_merge(torch.zeros(3, 2, 64), torch.zeros(3, 2, 2), None, torch.zeros(3, 64))
     with pytest.raises(ValueError):
-        K.kv_attn_decode(q, k, k, None, ctx, out, num_kv_heads=2, k_strides=(2 * 8 * 64, 64, 8 * 64),
-                         v_strides=(2 * 8 * 64, 64, 8 * 64), block_size=9, num_blocks=2, max_ctx_len=8)
+        E.kv_evict_select(torch.zeros(2, 2, 16), 8)
+    with pytest.raises(ValueError):
+        K.kv_attn_read_probe(torch.zeros(1024, dtype=torch.uint8), torch.zeros(1, dtype=torch.int32))
 
 
 def test_append_argument_errors_fail_before_any_hip_call():
